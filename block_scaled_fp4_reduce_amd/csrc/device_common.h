@@ -1,0 +1,123 @@
+// device_common.h -- gfx950 device helpers shared by the quantizer kernels.
+//
+// Number formats ("Four Over Six", sec. 1 and 2.1; NVIDIA NVFP4 article,
+// sec. 1): FP4 E2M1 values +-{0,.5,1,1.5,2,3,4,6}; FP8 E4M3 block scales
+// (bias 7, max 448); UE8M0 power-of-two scales for MXFP4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4q {
+
+constexpr int kThreads = 256;             // 4 wave64s per workgroup
+
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16
+// bf16 -> fp32 is exact: the bf16 bits are the upper half of the fp32 bits.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* y) {
+  y[0] = bf16_lo(v.x); y[1] = bf16_hi(v.x);
+  y[2] = bf16_lo(v.y); y[3] = bf16_hi(v.y);
+  y[4] = bf16_lo(v.z); y[5] = bf16_hi(v.z);
+  y[6] = bf16_lo(v.w); y[7] = bf16_hi(v.w);
+}
+
+// ---------------------------------------------------------------- E4M3
+// Nearest-even rounding of x >= 0 to E4M3, saturating at 448 (code 0x7E).
+// Normal range: round the fp32 mantissa to 3 bits on the bit pattern and
+// rebias the exponent from 127 to 7.  Below 2^-6 the step is 2^-9, so the
+// code is x * 512 rounded to an integer.  Negative and NaN inputs give 0.
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  uint32_t normal = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
+  normal = normal < 0x7Eu ? normal : 0x7Eu;
+  const float sub = fmaxf(__builtin_rintf(x * 512.0f), 0.0f);
+  return x >= 0x1p-6f ? normal : (uint32_t)sub;
+}
+
+// E4M3 code (0..126) -> value; exact.
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = code >> 3, m = code & 7u;
+  return e ? __builtin_ldexpf((float)(8u + m), (int)e - 10) : __builtin_ldexpf((float)m, -9);
+}
+
+// ---------------------------------------------------------------- E2M1
+// Hardware conversions of gfx950.  The scale operand carries an E8M0
+// exponent in the fp32 exponent field: 1.0f means "no scaling", and
+// __uint_as_float(code << 23) divides (encode) or multiplies (decode) by
+// 2^(code - 127) exactly.  Rounding is nearest-even, saturating at 6.
+template <int BYTE>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, BYTE);
+}
+
+template <int BYTE>
+__device__ __forceinline__ float2_t fp4x2_to_f32(uint32_t packed, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, scale, BYTE);
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror, Shaw (SC'11).  Returns output word 0 only; the
+// compiler drops the work the last rounds spend on the other words.
+__device__ __forceinline__ uint32_t philox_w0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                             uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// ---------------------------------------------------------------- Hadamard
+// Unnormalised Walsh-Hadamard butterfly (natural order): stage h pairs
+// (j, j+h) for j with bit h clear into (sum, difference).  N = 16 or 32.
+template <int N>
+__device__ __forceinline__ void fwht(float* v) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < N; j++) {
+      if (j & h) continue;
+      const float a = v[j], b = v[j + h];
+      v[j] = a + b;
+      v[j + h] = a - b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- wave/workgroup max
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
+    m = m > o ? m : o;
+  }
+  return m;
+}
+
+// Max over the workgroup (kThreads threads); every thread gets the result.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t* red /* [kThreads/64] */) {
+  m = wave_max_u32(m);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; w++) r = r > red[w] ? r : red[w];
+  return r;
+}
+
+}  // namespace fp4q

@@ -1,0 +1,211 @@
+// fp4q.hip -- C ABI of libfp4q.so: argument checks on the host, then kernel
+// launches on the caller's stream.  See include/fp4q.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include "../../include/fp4q.h"
+#include "mx_kernels.h"
+#include "nvfp4_2d_kernels.h"
+#include "nvfp4_kernels.h"
+
+using namespace fp4q;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr uint32_t kNvfp4Flags =
+    FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16 | FP4_BLOCK2D | FP4_ROWWISE | FP4_COLWISE;
+constexpr uint32_t kMxFlags = FP4_HAD32 | FP4_ROWWISE | FP4_COLWISE;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int check_shape(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return FP4_E_SHAPE;
+  if (rows > 0 && cols > 0 && (rows >= kMaxElems || cols >= kMaxElems || rows * cols >= kMaxElems))
+    return FP4_E_SHAPE;
+  return FP4_OK;
+}
+
+int check_nvfp4_flags(uint32_t flags) {
+  if (flags & ~kNvfp4Flags) return FP4_E_FLAGS;
+  if ((flags & FP4_SR) && (flags & FP4_FOUR_OVER_SIX)) return FP4_E_FLAGS;
+  if ((flags & FP4_BLOCK2D) && (flags & (FP4_SR | FP4_RHT16))) return FP4_E_FLAGS;
+  if ((flags & FP4_COLWISE) && !(flags & FP4_BLOCK2D)) return FP4_E_FLAGS;
+  return FP4_OK;
+}
+
+int amax_groups(int64_t ngroups16) {
+  const int64_t per_group = (int64_t)kThreads * kAmaxUnroll;   // uint4 loads per workgroup pass
+  int64_t g = cdiv(ngroups16 * 2, per_group);
+  if (g < 1) g = 1;
+  if (g > kAmaxMaxGroups) g = kAmaxMaxGroups;
+  return (int)g;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? FP4_OK : FP4_E_HIP; }
+
+// Queue the amax pass: partial maxima into ws (as uint32), `groups` of them.
+void launch_amax_partial(const uint16_t* x, int64_t ngroups16, uint32_t flags, uint64_t seed,
+                         uint32_t* ws, int groups, hipStream_t st) {
+  const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
+  if (flags & FP4_RHT16)
+    amax_partial_kernel<true><<<groups, kThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
+  else
+    amax_partial_kernel<false><<<groups, kThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
+}
+
+template <bool F46, bool SR, bool RHT>
+void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int namax,
+               float* alpha_out, uint8_t* codes, uint8_t* scales, uint8_t* choice,
+               uint64_t seed, hipStream_t st) {
+  const int64_t grid = nblocks > 0 ? cdiv(nblocks, kThreads) : 1;
+  nvfp4_1d_kernel<F46, SR, RHT><<<(unsigned)grid, kThreads, 0, st>>>(
+      (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
+      (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4_abi_version(void) { return 1; }
+
+const char* fp4_status_str(int status) {
+  switch (status) {
+    case FP4_OK: return "ok";
+    case FP4_E_NULL: return "a required pointer is NULL";
+    case FP4_E_SHAPE: return "shape not supported (negative, not a block multiple, or too large)";
+    case FP4_E_ALIGN: return "pointer misaligned (tensors and code buffers need 16-byte alignment)";
+    case FP4_E_FLAGS: return "unsupported flag combination";
+    case FP4_E_WORKSPACE: return "workspace smaller than fp4_workspace_bytes()";
+    case FP4_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t fp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
+  (void)rows; (void)cols;
+  if (flags & FP4_HAD32) return 0;
+  return (size_t)kAmaxMaxGroups * sizeof(uint32_t);
+}
+
+int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                    uint64_t seed, float* amax_out, void* ws, size_t ws_bytes, void* stream) {
+  const int64_t n = rows * cols;
+  if (!amax_out || !ws || (n > 0 && !x)) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  if (cols % 16) return FP4_E_SHAPE;
+  if (int rc = check_nvfp4_flags(flags)) return rc;
+  if (!aligned(x, 16) || !aligned(amax_out, 4) || !aligned(ws, 4)) return FP4_E_ALIGN;
+  if (ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t ng = n / 16;
+  const int groups = amax_groups(ng);
+  launch_amax_partial(x, ng, flags, seed, (uint32_t*)ws, groups, st);
+  amax_finalize_kernel<<<1, kThreads, 0, st>>>((const uint32_t*)ws, groups, amax_out);
+  return launched();
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                   const float* amax_in, float* alpha_out, uint8_t* codes, uint8_t* scales,
+                   uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t, void* ws,
+                   size_t ws_bytes, void* stream) {
+  const int64_t n = rows * cols;
+  const bool two_d = (flags & FP4_BLOCK2D) != 0;
+  const bool want_t = two_d && (flags & FP4_COLWISE);
+  if (!alpha_out) return FP4_E_NULL;
+  if (n > 0 && (!x || !codes || !scales)) return FP4_E_NULL;
+  if (n > 0 && want_t && (!codes_t || !scales_t)) return FP4_E_NULL;
+  if (!amax_in && !ws) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  if (cols % 16 || (two_d && rows % 16)) return FP4_E_SHAPE;
+  if (int rc = check_nvfp4_flags(flags)) return rc;
+  if (two_d && !kHave2D) return FP4_E_FLAGS;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(alpha_out, 4) || !aligned(amax_in, 4) ||
+      !aligned(ws, 4) || (want_t && !aligned(codes_t, 16)))
+    return FP4_E_ALIGN;
+  if (!amax_in && ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nblocks = n / 16;
+  const uint32_t* abits = (const uint32_t*)amax_in;
+  int namax = 1;
+  if (!amax_in) {
+    namax = amax_groups(nblocks);
+    launch_amax_partial(x, nblocks, flags, seed, (uint32_t*)ws, namax, st);
+    abits = (const uint32_t*)ws;
+  }
+  if (two_d) {
+    const bool f46 = (flags & FP4_FOUR_OVER_SIX) != 0;
+    launch_nvfp4_2d(x, rows, cols, f46, abits, namax, alpha_out, codes, scales, choice,
+                    want_t ? codes_t : nullptr, want_t ? scales_t : nullptr, st);
+    return launched();
+  }
+  const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
+  if (f46 && rht)
+    launch_1d<true, false, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  else if (f46)
+    launch_1d<true, false, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  else if (sr && rht)
+    launch_1d<false, true, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  else if (sr)
+    launch_1d<false, true, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  else if (rht)
+    launch_1d<false, false, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  else
+    launch_1d<false, false, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  return launched();
+}
+
+int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                   uint8_t* codes_r, uint8_t* scales_r, uint8_t* codes_c, uint8_t* scales_c,
+                   void* stream) {
+  const int64_t n = rows * cols;
+  const bool rw = flags & FP4_ROWWISE, cw = flags & FP4_COLWISE;
+  if (n > 0 && !x) return FP4_E_NULL;
+  if (n > 0 && rw && (!codes_r || !scales_r)) return FP4_E_NULL;
+  if (n > 0 && cw && (!codes_c || !scales_c)) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  if ((flags & ~kMxFlags) || !(rw || cw) || !kHaveMx) return FP4_E_FLAGS;
+  if (cols % 8 || (rw && cols % 32) || (cw && rows % 32)) return FP4_E_SHAPE;
+  if (!aligned(x, 16) || (rw && !aligned(codes_r, 16)) || (cw && !aligned(codes_c, 16)))
+    return FP4_E_ALIGN;
+  if (n == 0) return FP4_OK;
+  launch_mxfp4(x, rows, cols, (flags & FP4_HAD32) != 0, rw ? codes_r : nullptr,
+               rw ? scales_r : nullptr, cw ? codes_c : nullptr, cw ? scales_c : nullptr,
+               (hipStream_t)stream);
+  return launched();
+}
+
+int fp4_dequantize(int format, const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                   int64_t rows, int64_t cols, uint32_t flags, float* out, void* stream) {
+  const int64_t n = rows * cols;
+  if (format != FP4_FORMAT_NVFP4 && format != FP4_FORMAT_MXFP4) return FP4_E_FLAGS;
+  if (n > 0 && (!codes || !scales || !out)) return FP4_E_NULL;
+  if (format == FP4_FORMAT_NVFP4 && !alpha) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  const bool two_d = (flags & FP4_BLOCK2D) != 0;
+  if (format == FP4_FORMAT_NVFP4) {
+    if (flags & ~(uint32_t)FP4_BLOCK2D) return FP4_E_FLAGS;
+    if (cols % 16 || (two_d && rows % 16)) return FP4_E_SHAPE;
+  } else {
+    if (flags) return FP4_E_FLAGS;
+    if (cols % 32) return FP4_E_SHAPE;
+  }
+  if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(alpha, 4)) return FP4_E_ALIGN;
+  if (n == 0) return FP4_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (format == FP4_FORMAT_NVFP4) {
+    const int64_t nb = n / 16;
+    nvfp4_dequant_kernel<<<(unsigned)cdiv(nb, kThreads), kThreads, 0, st>>>(
+        (const uint2*)codes, scales, alpha, nb, cols / 16, two_d, (float4*)out);
+  } else {
+    const int64_t ng = n / 32;
+    mxfp4_dequant_kernel<<<(unsigned)cdiv(ng, kThreads), kThreads, 0, st>>>(
+        (const uint4*)codes, scales, ng, (float4*)out);
+  }
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+// nvfp4_2d_kernels.h -- NVFP4 with one E4M3 scale per 16x16 tile (weights),
+// optional Four Over Six, optional transposed output.
+//
+// Method: NVIDIA NVFP4 article sec. 2 and sec. 7 (2D block scaling keeps W
+// and W^T quantized identically, as the chain rule needs); "Four Over Six"
+// sec. 1 (per-block choice between scaling the max to 6 or to 4).
+//
+// Mapping onto the chip: 16 consecutive lanes hold one tile, one tile row
+// per lane (32 B of bf16, two 16-byte loads).  A wave covers 16 rows x 64
+// columns (4 tiles side by side: each row segment is one 128-byte line); a
+// workgroup's 4 waves stack to 64 rows and walk 4 such strips to the right.
+// The tile maximum and the 4/6 error sum are xor-butterflies over the 16
+// lanes (offsets 1, 2, 4, 8), i.e. a pairwise tree over the 16 row errors
+// whose result is bit-identical in every lane.  The transposed codes are
+// recomputed from an LDS copy of the tile with the same scale, so they are
+// the same fp32 operations on the same values and equal the row-wise codes
+// by construction.
+#pragma once
+
+#include "device_common.h"
+#include "nvfp4_kernels.h"
+
+namespace fp4q {
+
+constexpr bool kHave2D = true;
+constexpr int k2dStrips = 4;                 // 64-column strips per workgroup
+constexpr int k2dTileLds = 16 * 16 + 16;     // bf16 per tile in LDS (+32 B pad: no bank conflicts)
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  return __int_as_float(__shfl_xor(__float_as_int(v), m, 16));
+}
+
+// Max / sum over the 16 lanes of a tile, same bits in every lane.
+__device__ __forceinline__ float tile_max(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 1));
+  v = fmaxf(v, shfl_xor_f(v, 2));
+  v = fmaxf(v, shfl_xor_f(v, 4));
+  return fmaxf(v, shfl_xor_f(v, 8));
+}
+
+__device__ __forceinline__ float tile_sum(float v) {
+  v = v + shfl_xor_f(v, 1);
+  v = v + shfl_xor_f(v, 2);
+  v = v + shfl_xor_f(v, 4);
+  return v + shfl_xor_f(v, 8);
+}
+
+template <bool FOUR_SIX, bool TRANSPOSE>
+__global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+    const uint32_t* __restrict__ amax_bits, int namax, float* __restrict__ alpha_out,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ choice,
+    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
+  __shared__ float2 tab[128];
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint16_t stage[kThreads / 64][4][k2dTileLds];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = lane >> 4, r = lane & 15;                 // tile in wave, row in tile
+  const int64_t bcols = cols / 16, brows = rows / 16;
+  const int64_t tiles_x = (bcols + 4 * k2dStrips - 1) / (4 * k2dStrips);
+  const int64_t wg_y = blockIdx.x / tiles_x, wg_x = blockIdx.x - wg_y * tiles_x;
+  const int64_t br = wg_y * 4 + wave;                        // tile row of this wave
+  const bool row_ok = br < brows;
+  const int64_t row = br * 16 + r;
+
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < namax; i += kThreads) {
+    const uint32_t a = amax_bits[i];
+    m = m > a ? m : a;
+  }
+  m = block_max_u32(m, red);
+  const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_out = ts.alpha;
+  build_scale_table(tab, ts.alpha);
+  __syncthreads();
+
+  uint16_t* st = stage[wave][tile];
+  for (int s = 0; s < k2dStrips; s++) {
+    const int64_t bc = (wg_x * k2dStrips + s) * 4 + tile;   // tile column
+    const bool ok = row_ok && bc < bcols;
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+    if (ok) {
+      const uint4* src = (const uint4*)(x + row * cols + bc * 16);
+      v0 = src[0];
+      v1 = src[1];
+    }
+    float y[16];
+    unpack8(v0, y);
+    unpack8(v1, y + 8);
+    float amax_r = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; k++) amax_r = fmaxf(amax_r, fabsf(y[k]));
+    const float amax_b = tile_max(amax_r);
+
+    const uint32_t e6 = e4m3_rne(amax_b * ts.k6);
+    float2 sr = tab[e6];
+    uint32_t w0, w1, scale = e6, pick4 = 0;
+    const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
+    if constexpr (FOUR_SIX) {
+      const uint32_t e4 = e4m3_rne(amax_b * ts.k4);
+      const float2 sr4 = tab[e4];
+      uint32_t u0, u1;
+      const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
+      if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
+        w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
+      }
+    }
+    if (ok) {
+      *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
+      if (r == 0) {
+        scales[br * bcols + bc] = (uint8_t)scale;
+        if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
+        if constexpr (TRANSPOSE) scales_t[bc * brows + br] = (uint8_t)scale;
+      }
+    }
+    if constexpr (TRANSPOSE) {
+      // stage the tile (bf16, row r at st[16 r]), then lane r takes column r
+      *(uint4*)(st + 16 * r) = v0;
+      *(uint4*)(st + 16 * r + 8) = v1;
+      __syncthreads();
+      float yc[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
+      const float rr = sr.y;
+      uint32_t t0 = 0, t1 = 0;
+      t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
+      t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
+      t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
+      t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
+      t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
+      t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
+      t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
+      t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
+      if (ok) *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
+      __syncthreads();
+    }
+  }
+}
+
+inline void launch_nvfp4_2d(const uint16_t* x, int64_t rows, int64_t cols, bool f46,
+                            const uint32_t* abits, int namax, float* alpha_out, uint8_t* codes,
+                            uint8_t* scales, uint8_t* choice, uint8_t* codes_t,
+                            uint8_t* scales_t, hipStream_t st) {
+  const int64_t bcols = cols / 16, brows = rows / 16;
+  const int64_t tiles_x = (bcols + 4 * k2dStrips - 1) / (4 * k2dStrips);
+  const int64_t tiles_y = (brows + 3) / 4;
+  int64_t grid = tiles_x * tiles_y;
+  if (grid < 1) grid = 1;
+  const bool tr = codes_t != nullptr;
+#define FP4Q_2D(F, T)                                                                   \
+  nvfp4_2d_kernel<F, T><<<(unsigned)grid, kThreads, 0, st>>>(                           \
+      x, rows, cols, abits, namax, alpha_out, codes, scales, choice, codes_t, scales_t)
+  if (f46 && tr) FP4Q_2D(true, true);
+  else if (f46) FP4Q_2D(true, false);
+  else if (tr) FP4Q_2D(false, true);
+  else FP4Q_2D(false, false);
+#undef FP4Q_2D
+}
+
+}  // namespace fp4q

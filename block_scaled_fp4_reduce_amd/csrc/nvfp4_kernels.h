@@ -1,0 +1,312 @@
+// nvfp4_kernels.h -- NVFP4 tensor amax and 1D block quantizer for gfx950.
+//
+// Method: "Four Over Six" (sec. 2.1, Eq. 1-3; sec. 1, Fig. 1 and the
+// worked example) and the NVIDIA NVFP4 pretraining article (sec. 2: random
+// Hadamard, stochastic rounding; sec. 6: global and local encode scales).
+//
+// Mapping onto the chip: one lane owns one 16-value block (32 bytes of
+// bf16 read as two 16-byte loads), so the per-block scale work is done once
+// per block and never shuffled; a wave covers 64 consecutive blocks, i.e.
+// 2 KiB of input, 512 B of codes and 64 scale bytes, each stored with one
+// coalesced instruction.  The tensor scale comes from the amax pass as a
+// small array of per-workgroup partial maxima that every workgroup reduces
+// itself while its own input loads are in flight.
+#pragma once
+
+#include "device_common.h"
+
+namespace fp4q {
+
+// ------------------------------------------------------------------ amax
+// Per-workgroup partial maxima of |x| (or of |RHT16(x)|), as fp32 bit
+// patterns: non-negative floats order like their bit patterns, so the max
+// is an exact, order-free integer max.
+constexpr int kAmaxMaxGroups = 512;
+constexpr int kAmaxUnroll = 4;
+
+template <bool RHT>
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
+    const uint4* __restrict__ x, int64_t ngroups16, uint32_t* __restrict__ partials,
+    uint32_t seed_lo, uint32_t seed_hi) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t m = 0;
+  if constexpr (!RHT) {
+    // magnitude bits of two bf16 per dword; packed 16-bit integer max
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 mm = {0, 0};
+    const int64_t nvec = ngroups16 * 2;            // 8 bf16 per uint4
+    for (int64_t i = g; i < nvec; i += stride * kAmaxUnroll) {
+      uint4 v[kAmaxUnroll];
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; u++) {
+        const int64_t j = i + u * stride;
+        v[u] = j < nvec ? x[j] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; u++) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const uint32_t a = w[k] & 0x7FFF7FFFu;
+          mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, a));
+        }
+      }
+    }
+    const uint32_t lo = mm.x, hi = mm.y;
+    m = (lo > hi ? lo : hi) << 16;
+  } else {
+    const uint32_t signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
+    float fm = 0.0f;
+    for (int64_t i = g; i < ngroups16; i += stride) {
+      const uint4 v0 = x[2 * i], v1 = x[2 * i + 1];
+      float y[16];
+      unpack8(v0, y);
+      unpack8(v1, y + 8);
+#pragma unroll
+      for (int k = 0; k < 16; k++)
+        y[k] = __uint_as_float(__float_as_uint(y[k]) ^ (((signs >> k) & 1u) << 31));
+      fwht<16>(y);
+#pragma unroll
+      for (int k = 0; k < 16; k++) fm = fmaxf(fm, fabsf(y[k] * 0.25f));
+    }
+    m = __float_as_uint(fm);
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// One workgroup: reduce the partials and store the amax as a float.
+__global__ __launch_bounds__(kThreads) void amax_finalize_kernel(
+    const uint32_t* __restrict__ partials, int n, float* __restrict__ amax_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = m > partials[i] ? m : partials[i];
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) *amax_out = __uint_as_float(m);
+}
+
+// ------------------------------------------------------------------ quantizer
+// Tensor-level constants derived from the tensor amax.
+struct TensorScale {
+  float alpha;   // decode scale, Eq. 1: amax / (6 * C)
+  float k6, k4;  // encode factors (6*C/M) / amax: the block scale before
+                 // E4M3 rounding is amax_b * k_M (Eq. 2 via the global
+                 // encode scale of the NVIDIA article, sec. 6)
+};
+
+__device__ __forceinline__ TensorScale tensor_scale(float amax, bool four_six) {
+  const float C = four_six ? 256.0f : 448.0f;
+  TensorScale t;
+  t.alpha = amax / (6.0f * C);
+  t.k6 = amax == 0.0f ? 0.0f : C / amax;
+  t.k4 = amax == 0.0f ? 0.0f : (1.5f * C) / amax;
+  return t;
+}
+
+// Scale table in LDS: for every E4M3 code, (s, r) = (alpha*Delta, 1/(alpha*Delta))
+// with r = 0 when s = 0.  Replaces two per-block divisions by one lookup.
+__device__ __forceinline__ void build_scale_table(float2* tab, float alpha) {
+  if (threadIdx.x < 128) {
+    const uint32_t code = threadIdx.x < 127 ? threadIdx.x : 126u;
+    const float s = alpha * e4m3_value(code);
+    tab[threadIdx.x] = make_float2(s, s == 0.0f ? 0.0f : 1.0f / s);
+  }
+}
+
+// Error of one dequantized pair against its inputs, accumulated with fma.
+template <int BYTE>
+__device__ __forceinline__ float err_pair(uint32_t packed, float s, float y0, float y1, float acc) {
+  const float2_t q = fp4x2_to_f32<BYTE>(packed, 1.0f);
+  const float d0 = __builtin_fmaf(q.x, s, -y0);
+  acc = __builtin_fmaf(d0, d0, acc);
+  const float d1 = __builtin_fmaf(q.y, s, -y1);
+  return __builtin_fmaf(d1, d1, acc);
+}
+
+// Nearest-even quantization of 16 values with encode scale r; returns the
+// two code dwords and the block's squared error of q*s against y, summed as
+// two fma chains (elements 0..7 and 8..15) that are then added.
+__device__ __forceinline__ float quant16_rtn(const float* y, float s, float r, uint32_t& w0,
+                                             uint32_t& w1) {
+  w0 = 0; w1 = 0;
+  w0 = cvt_fp4x2<0>(w0, y[0] * r, y[1] * r, 1.0f);
+  w0 = cvt_fp4x2<1>(w0, y[2] * r, y[3] * r, 1.0f);
+  w0 = cvt_fp4x2<2>(w0, y[4] * r, y[5] * r, 1.0f);
+  w0 = cvt_fp4x2<3>(w0, y[6] * r, y[7] * r, 1.0f);
+  w1 = cvt_fp4x2<0>(w1, y[8] * r, y[9] * r, 1.0f);
+  w1 = cvt_fp4x2<1>(w1, y[10] * r, y[11] * r, 1.0f);
+  w1 = cvt_fp4x2<2>(w1, y[12] * r, y[13] * r, 1.0f);
+  w1 = cvt_fp4x2<3>(w1, y[14] * r, y[15] * r, 1.0f);
+  float lo = 0.0f, hi = 0.0f;
+  lo = err_pair<0>(w0, s, y[0], y[1], lo);
+  lo = err_pair<1>(w0, s, y[2], y[3], lo);
+  lo = err_pair<2>(w0, s, y[4], y[5], lo);
+  lo = err_pair<3>(w0, s, y[6], y[7], lo);
+  hi = err_pair<0>(w1, s, y[8], y[9], hi);
+  hi = err_pair<1>(w1, s, y[10], y[11], hi);
+  hi = err_pair<2>(w1, s, y[12], y[13], hi);
+  hi = err_pair<3>(w1, s, y[14], y[15], hi);
+  return lo + hi;
+}
+
+// Stochastic rounding of t onto the FP4 grid: between neighbours lo <= |t| < hi
+// round up iff u < (|t| - lo)/(hi - lo), u = (philox word 0 >> 8) * 2^-24 for
+// counter = element index.  Returns the signed grid value.
+__device__ __forceinline__ float sr_value(float t, uint64_t idx, uint32_t k0, uint32_t k1) {
+  const uint32_t w = philox_w0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, k0, k1);
+  const float u = (float)(w >> 8) * 0x1p-24f;
+  const float a = fabsf(t);
+  float mag;
+  if (!(a < 6.0f)) {
+    mag = 6.0f;
+  } else {
+    const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+    const float lo = a < 2.0f ? __builtin_floorf(a * 2.0f) * 0.5f
+                              : (a < 4.0f ? __builtin_floorf(a) : 4.0f);
+    const float p = (a - lo) / step;
+    mag = u < p ? lo + step : lo;
+  }
+  return __builtin_copysignf(mag, t);
+}
+
+__device__ __forceinline__ float quant16_sr(const float* y, float s, float r, uint64_t idx0,
+                                            uint32_t k0, uint32_t k1, uint32_t& w0, uint32_t& w1) {
+  float q[16];
+#pragma unroll
+  for (int i = 0; i < 16; i++) q[i] = sr_value(y[i] * r, idx0 + i, k0, k1);
+  // grid values convert exactly
+  w0 = 0; w1 = 0;
+  w0 = cvt_fp4x2<0>(w0, q[0], q[1], 1.0f);
+  w0 = cvt_fp4x2<1>(w0, q[2], q[3], 1.0f);
+  w0 = cvt_fp4x2<2>(w0, q[4], q[5], 1.0f);
+  w0 = cvt_fp4x2<3>(w0, q[6], q[7], 1.0f);
+  w1 = cvt_fp4x2<0>(w1, q[8], q[9], 1.0f);
+  w1 = cvt_fp4x2<1>(w1, q[10], q[11], 1.0f);
+  w1 = cvt_fp4x2<2>(w1, q[12], q[13], 1.0f);
+  w1 = cvt_fp4x2<3>(w1, q[14], q[15], 1.0f);
+  (void)s;
+  return 0.0f;
+}
+
+// 1D NVFP4: one lane per 16-value block of the flattened tensor (blocks never
+// straddle rows because cols % 16 == 0).
+//   amax_bits/namax: values whose max is the tensor amax (fp32 bit patterns):
+//   the amax pass partials, or the caller's amax_in (namax = 1).
+template <bool FOUR_SIX, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, const uint32_t* __restrict__ amax_bits,
+    int namax, float* __restrict__ alpha_out, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint8_t* __restrict__ choice, uint32_t seed_lo,
+    uint32_t seed_hi) {
+  __shared__ float2 tab[128];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool active = b < nblocks;
+
+  // input loads first: they do not depend on the tensor scale
+  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  if (active) {
+    v0 = x[2 * b];
+    v1 = x[2 * b + 1];
+  }
+
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < namax; i += kThreads) {
+    const uint32_t a = amax_bits[i];
+    m = m > a ? m : a;
+  }
+  m = block_max_u32(m, red);
+  const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_out = ts.alpha;
+  build_scale_table(tab, ts.alpha);
+  __syncthreads();
+  if (!active) return;
+
+  float y[16];
+  unpack8(v0, y);
+  unpack8(v1, y + 8);
+  if constexpr (RHT) {
+    const uint32_t signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+      y[k] = __uint_as_float(__float_as_uint(y[k]) ^ (((signs >> k) & 1u) << 31));
+    fwht<16>(y);
+#pragma unroll
+    for (int k = 0; k < 16; k++) y[k] = y[k] * 0.25f;
+  }
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k++) amax_b = fmaxf(amax_b, fabsf(y[k]));
+
+  const uint32_t e6 = e4m3_rne(amax_b * ts.k6);
+  const float2 sr6 = tab[e6];
+  uint32_t w0, w1, scale = e6, pick4 = 0;
+  if constexpr (SR) {
+    quant16_sr(y, sr6.x, sr6.y, (uint64_t)b * 16, seed_lo, seed_hi, w0, w1);
+  } else {
+    const float err6 = quant16_rtn(y, sr6.x, sr6.y, w0, w1);
+    if constexpr (FOUR_SIX) {
+      const uint32_t e4 = e4m3_rne(amax_b * ts.k4);
+      const float2 sr4 = tab[e4];
+      uint32_t u0, u1;
+      const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
+      if (err4 < err6) {  // ties keep M = 6
+        w0 = u0; w1 = u1; scale = e4; pick4 = 1;
+      }
+    }
+  }
+  codes[b] = make_uint2(w0, w1);
+  scales[b] = (uint8_t)scale;
+  if (choice) choice[b] = (uint8_t)pick4;
+}
+
+// ------------------------------------------------------------------ dequantize
+// NVFP4: out = q * (alpha * Delta); one lane per 16 values.
+__global__ __launch_bounds__(kThreads) void nvfp4_dequant_kernel(
+    const uint2* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ alpha, int64_t nblocks, int64_t bcols, bool two_d,
+    float4* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblocks) return;
+  const int64_t row = b / bcols, bc = b - row * bcols;
+  const int64_t sidx = two_d ? (row / 16) * bcols + bc : b;
+  const float s = alpha[0] * e4m3_value(scales[sidx] & 0x7Fu);
+  const uint2 c = codes[b];
+  float q[16];
+  float2_t t;
+  t = fp4x2_to_f32<0>(c.x, 1.0f); q[0] = t.x; q[1] = t.y;
+  t = fp4x2_to_f32<1>(c.x, 1.0f); q[2] = t.x; q[3] = t.y;
+  t = fp4x2_to_f32<2>(c.x, 1.0f); q[4] = t.x; q[5] = t.y;
+  t = fp4x2_to_f32<3>(c.x, 1.0f); q[6] = t.x; q[7] = t.y;
+  t = fp4x2_to_f32<0>(c.y, 1.0f); q[8] = t.x; q[9] = t.y;
+  t = fp4x2_to_f32<1>(c.y, 1.0f); q[10] = t.x; q[11] = t.y;
+  t = fp4x2_to_f32<2>(c.y, 1.0f); q[12] = t.x; q[13] = t.y;
+  t = fp4x2_to_f32<3>(c.y, 1.0f); q[14] = t.x; q[15] = t.y;
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    out[4 * b + k] = make_float4(q[4 * k] * s, q[4 * k + 1] * s, q[4 * k + 2] * s, q[4 * k + 3] * s);
+}
+
+// MXFP4: out = q * 2^(code - 127); one lane per 32 values.
+__global__ __launch_bounds__(kThreads) void mxfp4_dequant_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t ngroups,
+    float4* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= ngroups) return;
+  const uint32_t sc = scales[g];
+  // 2^(sc-127) as a float; sc = 0 is the subnormal 2^-127
+  const float s = sc ? __uint_as_float(sc << 23) : __uint_as_float(0x00400000u);
+  const uint4 c = codes[g];
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const float2_t a = fp4x2_to_f32<0>(w[k], 1.0f), b2 = fp4x2_to_f32<1>(w[k], 1.0f);
+    const float2_t c2 = fp4x2_to_f32<2>(w[k], 1.0f), d = fp4x2_to_f32<3>(w[k], 1.0f);
+    out[8 * g + 2 * k] = make_float4(a.x * s, a.y * s, b2.x * s, b2.y * s);
+    out[8 * g + 2 * k + 1] = make_float4(c2.x * s, c2.y * s, d.x * s, d.y * s);
+  }
+}
+
+}  // namespace fp4q

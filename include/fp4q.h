@@ -1,0 +1,156 @@
+/*
+ * fp4q.h -- block-scaled FP4 quantization of bf16 tensors on AMD MI355X
+ * (gfx950).  C ABI of libfp4q.so.
+ *
+ * The method (cited by page title and section):
+ *  - NVFP4: FP4 E2M1 values, one FP8 E4M3 scale per 16 consecutive values
+ *    and one FP32 tensor scale ("Four Over Six: More Accurate NVFP4
+ *    Quantization with Adaptive Block Scaling", sec. 2.1, Eq. 1-3; NVIDIA
+ *    NVFP4 pretraining article, sec. 1 and sec. 6).
+ *  - Four Over Six: per 16-value block, quantize with the block maximum
+ *    scaled to 6 and to 4 and keep the one with the smaller error ("Four
+ *    Over Six", sec. 1, Fig. 1 and the worked example).
+ *  - Variants for the tensors of a training step (NVIDIA NVFP4 article,
+ *    sec. 2 and sec. 7): a 16-point random Hadamard rotation and stochastic
+ *    rounding for gradients, 16x16 two-dimensional blocks for weights.
+ *  - MXFP4: 32 values per power-of-two (UE8M0) scale (NVIDIA NVFP4 article,
+ *    sec. 1 and sec. 5), with a fixed 32-point Hadamard rotation (AMD
+ *    MI355X MXFP4 pretraining article, sec. 2) and row- and column-wise
+ *    outputs.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor pointer is a DEVICE pointer (HIP device memory of the
+ *    current device).  The caller allocates every buffer and owns it; the
+ *    library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is queued on it asynchronously; the call returns before the GPU
+ *    finishes.  Concurrent calls on different streams are safe as long as
+ *    they do not share output or workspace buffers.
+ *  - Inputs are row-major bf16 bit patterns [rows][cols], 16-byte aligned.
+ *  - Packed FP4 codes: two per byte, the even-indexed element in the low
+ *    nibble; code = sign << 3 | magnitude index into {0, .5, 1, 1.5, 2, 3,
+ *    4, 6}.  Code buffers must be 16-byte aligned.
+ *  - Scales are one byte per block in row-major block order; NVFP4 scales
+ *    are E4M3 (bias 7, max 448), MXFP4 scales are UE8M0 (2^(code-127)).
+ *  - Errors: the return value is an fp4_status.  Argument checks run on the
+ *    host before any HIP call, so a rejected call touches no device state.
+ *    FP4_E_HIP reports a failed kernel launch (hipGetLastError); faults
+ *    during execution surface at the caller's next synchronisation.
+ *  - Tensors holding Inf/NaN, or (NVFP4) whose largest magnitude is below
+ *    2^-64 without being zero, are outside the method's domain: the call
+ *    succeeds and never faults, but codes and scales are unspecified.
+ */
+#ifndef FP4Q_H
+#define FP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_E_NULL = -1,      /* a required pointer is NULL                     */
+  FP4_E_SHAPE = -2,     /* rows/cols negative, not a block multiple, or
+                           rows*cols >= 2^40                              */
+  FP4_E_ALIGN = -3,     /* a pointer breaks the alignment rules above     */
+  FP4_E_FLAGS = -4,     /* unknown bit or an unsupported combination      */
+  FP4_E_WORKSPACE = -5, /* workspace smaller than fp4_workspace_bytes()   */
+  FP4_E_HIP = -6        /* kernel launch failed                           */
+} fp4_status;
+
+/* Mode flags. */
+enum {
+  FP4_RTN6 = 0u,               /* NVFP4, block max scaled to 6, nearest-even  */
+  FP4_FOUR_OVER_SIX = 1u << 0, /* NVFP4: adaptive choice of 6 or 4 per block  */
+  FP4_SR = 1u << 1,            /* NVFP4: stochastic rounding of FP4 values    */
+  FP4_RHT16 = 1u << 2,         /* NVFP4: 16-point random Hadamard along rows  */
+  FP4_BLOCK2D = 1u << 3,       /* NVFP4: 16x16 tiles instead of 1x16 blocks   */
+  FP4_HAD32 = 1u << 4,         /* MXFP4: 32-point Hadamard before quantizing  */
+  FP4_ROWWISE = 1u << 5,       /* MXFP4: emit row-wise output                 */
+  FP4_COLWISE = 1u << 6        /* MXFP4: emit column-wise output;
+                                  NVFP4 2D: also emit the transpose          */
+};
+
+enum { FP4_FORMAT_NVFP4 = 0, FP4_FORMAT_MXFP4 = 1 };
+
+/* Bytes of device workspace nvfp4_quantize (with amax_in == NULL) and
+ * fp4_tensor_amax need for this shape and these flags; 0 if none.  The
+ * workspace needs no initialisation and is scratch for the duration of the
+ * call (stream order). */
+size_t fp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);
+
+/* Largest magnitude of the tensor the NVFP4 quantizer scales by ("Four Over
+ * Six" Eq. 1 numerator; NVIDIA NVFP4 article sec. 6 and sec. 9: the extra
+ * pass over memory for the global scale).  With FP4_RHT16 it is the
+ * largest magnitude after the rotation (seeded by `seed`).  Other NVFP4 flag
+ * bits are accepted and ignored; FP4_HAD32 is rejected.
+ *   x        [rows][cols] bf16, cols % 16 == 0
+ *   amax_out one float (device), written in stream order
+ *   ws       fp4_workspace_bytes(rows, cols, flags) bytes (device) */
+int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols,
+                    uint32_t flags, uint64_t seed, float* amax_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* NVFP4 quantization ("Four Over Six" Eq. 1-3 and sec. 1; NVIDIA NVFP4
+ * article sec. 2 and sec. 6).
+ *   flags     FP4_RTN6 or any of FOUR_OVER_SIX, SR, RHT16, BLOCK2D
+ *             (+ COLWISE with BLOCK2D).  Rejected: SR|FOUR_OVER_SIX,
+ *             BLOCK2D|SR, BLOCK2D|RHT16, HAD32, COLWISE without BLOCK2D.
+ *   seed      Philox key for SR (counter = row*cols + col) and RHT16 signs.
+ *   amax_in   NULL: computed here (one extra read of x, needs `ws`);
+ *             else one device float taken as the tensor's largest magnitude.
+ *   alpha_out one device float: the FP32 tensor scale amax/(6*C), C = 448,
+ *             or 256 with FOUR_OVER_SIX.
+ *   codes     [rows][cols/2] bytes.
+ *   scales    E4M3, [rows][cols/16] (1D) or [rows/16][cols/16] (BLOCK2D).
+ *   choice    NULL or one byte per scale, 1 where the block took M = 4.
+ *   codes_t, scales_t  BLOCK2D|COLWISE only (else NULL): the same
+ *             quantization laid out for the transpose, [cols][rows/2] and
+ *             [cols/16][rows/16].
+ *   Shapes: cols % 16 == 0; BLOCK2D also rows % 16 == 0. */
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
+                   uint32_t flags, uint64_t seed, const float* amax_in,
+                   float* alpha_out, uint8_t* codes, uint8_t* scales,
+                   uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP4 quantization (NVIDIA NVFP4 article sec. 1 and 5; AMD MI355X MXFP4
+ * article sec. 2).  Per 32 values: optional 32-point Hadamard (FP4_HAD32,
+ * orthonormal), exponent e = floor(log2(amax)) - 2 (UE8M0 code e + 127,
+ * 0 for an all-zero group), values scaled by 2^-e and rounded to nearest
+ * even E2M1, saturating at 6.
+ *   flags     HAD32 optional; ROWWISE and/or COLWISE (at least one).
+ *   codes_r   [rows][cols/2], scales_r [rows][cols/32]   (ROWWISE, cols % 32 == 0)
+ *   codes_c   [cols][rows/2], scales_c [cols][rows/32]   (COLWISE, rows % 32 == 0):
+ *             the row-wise quantization of the transpose; the rotation and
+ *             the 32-value groups run down the columns.
+ *   Shapes: cols % 8 == 0 always (16-byte rows), plus the multiples above.
+ *   Unused outputs may be NULL. */
+int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
+                   uint32_t flags, uint8_t* codes_r, uint8_t* scales_r,
+                   uint8_t* codes_c, uint8_t* scales_c, void* stream);
+
+/* Dequantize to fp32 [rows][cols] (the decode applied by the consumer:
+ * NVIDIA NVFP4 article sec. 4 and sec. 6).
+ *   format FP4_FORMAT_NVFP4: out = q * (alpha * Delta), alpha = *alpha
+ *          (device float); flags FP4_BLOCK2D selects 16x16 tiles.
+ *   format FP4_FORMAT_MXFP4: out = q * 2^(code-127); alpha ignored (may be
+ *          NULL); pass (cols, rows) of the original to decode COLWISE output.
+ *   out    16-byte aligned. */
+int fp4_dequantize(int format, const uint8_t* codes, const uint8_t* scales,
+                   const float* alpha, int64_t rows, int64_t cols,
+                   uint32_t flags, float* out, void* stream);
+
+/* Static description of a status code. */
+const char* fp4_status_str(int status);
+
+/* Interface version (bumped on any incompatible change). */
+int fp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4Q_H */

@@ -1,0 +1,125 @@
+"""GPU parity of the 16x16-tile NVFP4 path and of MXFP4 (row- and
+column-wise, with and without the 32-point Hadamard) against the CPU oracle.
+Both sides run the same fp32 operations, so every code and scale must match
+bit for bit."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_scaled_fp4_reduce_amd as fp4  # noqa: E402
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def same(g, w, what):
+    g = host(g)
+    assert g.shape == w.shape, (what, g.shape, w.shape)
+    bad = np.argwhere(g != w)
+    assert bad.size == 0, "%s differs at %d places, first %s: gpu %s oracle %s" % (
+        what, len(bad), bad[:3].tolist(), g[tuple(bad[0])], w[tuple(bad[0])])
+
+
+# ------------------------------------------------------------ NVFP4 2D
+@pytest.mark.parametrize("flags", [fp4.BLOCK2D, fp4.BLOCK2D | fp4.FOUR_OVER_SIX,
+                                   fp4.BLOCK2D | fp4.COLWISE,
+                                   fp4.BLOCK2D | fp4.FOUR_OVER_SIX | fp4.COLWISE])
+@pytest.mark.parametrize("shape", [(16, 16), (80, 400), (272, 1040), (64, 4096)])
+def test_2d_parity(shape, flags):
+    x = S.gen("c3", *shape)
+    print("2d case", shape, flags, flush=True)
+    got = fp4.nvfp4_quantize(dev(x), flags, want_choice=True)
+    torch.cuda.synchronize()
+    want = O.nvfp4_quantize(x, flags)
+    same(got["codes"], want["codes"], "codes")
+    same(got["scales"], want["scales"], "scales")
+    assert host(got["alpha"])[0] == want["alpha"]
+    if flags & fp4.FOUR_OVER_SIX:
+        same(got["choice"], want["choice"], "choice")
+    if flags & fp4.COLWISE:
+        same(got["codes_t"], want["codes_t"], "codes_t")
+        same(got["scales_t"], want["scales_t"], "scales_t")
+
+
+def test_2d_special_values_and_dequant():
+    x = S.special_values_tensor(64, 96, seed=11)
+    f = fp4.BLOCK2D | fp4.FOUR_OVER_SIX | fp4.COLWISE
+    got = fp4.nvfp4_quantize(dev(x), f)
+    want = O.nvfp4_quantize(x, f)
+    same(got["codes"], want["codes"], "codes")
+    same(got["codes_t"], want["codes_t"], "codes_t")
+    d = fp4.fp4_dequantize(fp4.FORMAT_NVFP4, got["codes"], got["scales"], got["alpha"], 64, 96,
+                           fp4.BLOCK2D)
+    same(d, O.dequantize(0, want["codes"], want["scales"], want["alpha"], 64, 96, O.BLOCK2D),
+         "dequant")
+
+
+def test_2d_c3_full():
+    x = S.gen("c3")
+    f = fp4.BLOCK2D | fp4.FOUR_OVER_SIX | fp4.COLWISE
+    got = fp4.nvfp4_quantize(dev(x), f, want_choice=True)
+    want = O.nvfp4_quantize(x, f)
+    for k in ("codes", "scales", "choice", "codes_t", "scales_t"):
+        same(got[k], want[k], k)
+
+
+# ------------------------------------------------------------ MXFP4
+MX_FLAGS = [fp4.ROWWISE, fp4.COLWISE, fp4.ROWWISE | fp4.COLWISE,
+            fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE, fp4.HAD32 | fp4.COLWISE]
+
+
+@pytest.mark.parametrize("flags", MX_FLAGS)
+@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (160, 4128), (320, 256)])
+def test_mx_parity(shape, flags):
+    x = S.gen("c5", *shape)
+    print("mx case", shape, flags, flush=True)
+    got = fp4.mxfp4_quantize(dev(x), flags)
+    torch.cuda.synchronize()
+    want = O.mxfp4_quantize(x, flags)
+    for k in want:
+        same(got[k], want[k], k)
+
+
+def test_mx_special_values_subnormal_groups():
+    x = S.special_values_tensor(64, 128, seed=5)
+    x[:32, :32] = np.arange(1, 0x20 + 1, dtype=np.uint16)[None, :]    # subnormal-only group
+    x[32:64, 96:128] = 0x0001                                          # smallest subnormal
+    for flags in (fp4.ROWWISE | fp4.COLWISE, fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE):
+        got = fp4.mxfp4_quantize(dev(x), flags)
+        want = O.mxfp4_quantize(x, flags)
+        for k in want:
+            same(got[k], want[k], k)
+
+
+def test_mx_dequant_both_orientations():
+    x = S.gen("c5", 64, 96)
+    f = fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE
+    got = fp4.mxfp4_quantize(dev(x), f)
+    want = O.mxfp4_quantize(x, f)
+    dr = fp4.fp4_dequantize(fp4.FORMAT_MXFP4, got["codes_r"], got["scales_r"], None, 64, 96)
+    dc = fp4.fp4_dequantize(fp4.FORMAT_MXFP4, got["codes_c"], got["scales_c"], None, 96, 64)
+    same(dr, O.dequantize(1, want["codes_r"], want["scales_r"], 0.0, 64, 96), "dequant rows")
+    same(dc, O.dequantize(1, want["codes_c"], want["scales_c"], 0.0, 96, 64), "dequant cols")
+
+
+def test_mx_c5_full():
+    x = S.gen("c5")
+    f = fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE
+    got = fp4.mxfp4_quantize(dev(x), f)
+    torch.cuda.synchronize()
+    want = O.mxfp4_quantize(x, f)
+    for k in want:
+        same(got[k], want[k], k)
