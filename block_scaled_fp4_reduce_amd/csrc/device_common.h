@@ -108,15 +108,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
   return m;
 }
 
-// Max over the workgroup (kThreads threads); every thread gets the result.
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t* red /* [kThreads/64] */) {
+// Max over a workgroup of NT threads; every thread gets the result.
+template <int NT = kThreads>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t* red /* [NT/64] */) {
   m = wave_max_u32(m);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = m;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; w++) r = r > red[w] ? r : red[w];
+  for (int w = 1; w < NT / 64; w++) r = r > red[w] ? r : red[w];
   return r;
 }
 

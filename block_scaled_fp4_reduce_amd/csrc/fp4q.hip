@@ -36,7 +36,7 @@ int check_nvfp4_flags(uint32_t flags) {
 }
 
 int amax_groups(int64_t ngroups16) {
-  const int64_t per_group = (int64_t)kThreads * kAmaxUnroll;   // uint4 loads per workgroup pass
+  const int64_t per_group = (int64_t)kAmaxThreads * kAmaxUnroll;   // uint4 loads per workgroup pass
   int64_t g = cdiv(ngroups16 * 2, per_group);
   if (g < 1) g = 1;
   if (g > kAmaxMaxGroups) g = kAmaxMaxGroups;
@@ -45,21 +45,36 @@ int amax_groups(int64_t ngroups16) {
 
 int launched() { return hipGetLastError() == hipSuccess ? FP4_OK : FP4_E_HIP; }
 
+// Compute units of the current device (queried once per device; 256 on MI355X).
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 // Queue the amax pass: partial maxima into ws (as uint32), `groups` of them.
 void launch_amax_partial(const uint16_t* x, int64_t ngroups16, uint32_t flags, uint64_t seed,
                          uint32_t* ws, int groups, hipStream_t st) {
   const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
   if (flags & FP4_RHT16)
-    amax_partial_kernel<true><<<groups, kThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
+    amax_partial_kernel<true><<<groups, kAmaxThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
   else
-    amax_partial_kernel<false><<<groups, kThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
+    amax_partial_kernel<false><<<groups, kAmaxThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
 }
 
 template <bool F46, bool SR, bool RHT>
 void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int namax,
                float* alpha_out, uint8_t* codes, uint8_t* scales, uint8_t* choice,
                uint64_t seed, hipStream_t st) {
-  const int64_t grid = nblocks > 0 ? cdiv(nblocks, kThreads) : 1;
+  int64_t grid = nblocks > 0 ? cdiv(nblocks, (int64_t)kThreads) : 1;
+  if (grid > (int64_t)num_cus() * kWgPerCu) grid = (int64_t)num_cus() * kWgPerCu;
   nvfp4_1d_kernel<F46, SR, RHT><<<(unsigned)grid, kThreads, 0, st>>>(
       (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
       (uint32_t)seed, (uint32_t)(seed >> 32));

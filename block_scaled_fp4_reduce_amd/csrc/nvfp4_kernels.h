@@ -21,16 +21,37 @@ namespace fp4q {
 // Per-workgroup partial maxima of |x| (or of |RHT16(x)|), as fp32 bit
 // patterns: non-negative floats order like their bit patterns, so the max
 // is an exact, order-free integer max.
-constexpr int kAmaxMaxGroups = 512;
-constexpr int kAmaxUnroll = 4;
+#ifndef FP4Q_AMAX_GROUPS
+#define FP4Q_AMAX_GROUPS 256
+#endif
+#ifndef FP4Q_AMAX_THREADS
+#define FP4Q_AMAX_THREADS 1024
+#endif
+#ifndef FP4Q_AMAX_UNROLL
+#define FP4Q_AMAX_UNROLL 4
+#endif
+#ifndef FP4Q_BPT
+#define FP4Q_BPT 1
+#endif
+#ifndef FP4Q_WG_PER_CU
+#define FP4Q_WG_PER_CU 4
+#endif
+#ifndef FP4Q_HW_E4M3
+#define FP4Q_HW_E4M3 1
+#endif
+constexpr int kAmaxMaxGroups = FP4Q_AMAX_GROUPS;
+constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
+constexpr int kAmaxThreads = FP4Q_AMAX_THREADS;
+constexpr int kBpt = FP4Q_BPT;              // 16-value blocks per lane per chunk (1D quantizer)
+constexpr int kWgPerCu = FP4Q_WG_PER_CU;    // resident 1D-quantizer workgroups per CU
 
 template <bool RHT>
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
     const uint4* __restrict__ x, int64_t ngroups16, uint32_t* __restrict__ partials,
     uint32_t seed_lo, uint32_t seed_hi) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  int64_t g = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   uint32_t m = 0;
   if constexpr (!RHT) {
     // magnitude bits of two bf16 per dword; packed 16-bit integer max
@@ -73,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(
     }
     m = __float_as_uint(fm);
   }
-  m = block_max_u32(m, red);
+  m = block_max_u32<kAmaxThreads>(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
@@ -190,45 +211,35 @@ __device__ __forceinline__ float quant16_sr(const float* y, float s, float r, ui
   return 0.0f;
 }
 
-// 1D NVFP4: one lane per 16-value block of the flattened tensor (blocks never
-// straddle rows because cols % 16 == 0).
-//   amax_bits/namax: values whose max is the tensor amax (fp32 bit patterns):
-//   the amax pass partials, or the caller's amax_in (namax = 1).
+// E4M3 codes of two non-negative block scales.  The hardware conversion
+// (OCP E4M3, nearest-even) is used after a clamp to [0, 448], so values past
+// the largest finite E4M3 saturate; the result indexes the 128-entry scale
+// table (code 0x7F, unreachable for finite input, maps to a copy of 448).
+__device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t& ca, uint32_t& cb) {
+#if FP4Q_HW_E4M3
+  const float a2 = __builtin_amdgcn_fmed3f(a, 0.0f, 448.0f);
+  const float b2 = __builtin_amdgcn_fmed3f(b, 0.0f, 448.0f);
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, b2, 0, false);
+  ca = w & 0x7Fu;
+  cb = (w >> 8) & 0x7Fu;
+#else
+  ca = e4m3_rne(a);
+  cb = e4m3_rne(b);
+#endif
+}
+
+// Quantize one 16-value block (the lane's) and store codes, scale, choice.
 template <bool FOUR_SIX, bool SR, bool RHT>
-__global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, const uint32_t* __restrict__ amax_bits,
-    int namax, float* __restrict__ alpha_out, uint2* __restrict__ codes,
-    uint8_t* __restrict__ scales, uint8_t* __restrict__ choice, uint32_t seed_lo,
-    uint32_t seed_hi) {
-  __shared__ float2 tab[128];
-  __shared__ uint32_t red[kThreads / 64];
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool active = b < nblocks;
-
-  // input loads first: they do not depend on the tensor scale
-  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-  if (active) {
-    v0 = x[2 * b];
-    v1 = x[2 * b + 1];
-  }
-
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < namax; i += kThreads) {
-    const uint32_t a = amax_bits[i];
-    m = m > a ? m : a;
-  }
-  m = block_max_u32(m, red);
-  const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_out = ts.alpha;
-  build_scale_table(tab, ts.alpha);
-  __syncthreads();
-  if (!active) return;
-
+__device__ __forceinline__ void nvfp4_block(const uint4& v0, const uint4& v1, int64_t b,
+                                            const float2* tab, float k6, float k4,
+                                            uint32_t signs, uint32_t seed_lo, uint32_t seed_hi,
+                                            uint2* __restrict__ codes,
+                                            uint8_t* __restrict__ scales,
+                                            uint8_t* __restrict__ choice) {
   float y[16];
   unpack8(v0, y);
   unpack8(v1, y + 8);
   if constexpr (RHT) {
-    const uint32_t signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
 #pragma unroll
     for (int k = 0; k < 16; k++)
       y[k] = __uint_as_float(__float_as_uint(y[k]) ^ (((signs >> k) & 1u) << 31));
@@ -240,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
 #pragma unroll
   for (int k = 0; k < 16; k++) amax_b = fmaxf(amax_b, fabsf(y[k]));
 
-  const uint32_t e6 = e4m3_rne(amax_b * ts.k6);
+  uint32_t e6, e4;
+  e4m3_pair(amax_b * k6, amax_b * k4, e6, e4);
   const float2 sr6 = tab[e6];
   uint32_t w0, w1, scale = e6, pick4 = 0;
   if constexpr (SR) {
@@ -248,7 +260,6 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   } else {
     const float err6 = quant16_rtn(y, sr6.x, sr6.y, w0, w1);
     if constexpr (FOUR_SIX) {
-      const uint32_t e4 = e4m3_rne(amax_b * ts.k4);
       const float2 sr4 = tab[e4];
       uint32_t u0, u1;
       const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
@@ -260,6 +271,90 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   codes[b] = make_uint2(w0, w1);
   scales[b] = (uint8_t)scale;
   if (choice) choice[b] = (uint8_t)pick4;
+}
+
+// 1D NVFP4: one lane per 16-value block of the flattened tensor (blocks never
+// straddle rows because cols % 16 == 0).  Persistent workgroups walk chunks
+// of kThreads blocks with a stride of the grid, with two register buffers:
+// chunk i+1 is loaded while chunk i is computed, so memory and VALU work
+// overlap and the tensor-scale prologue runs once per workgroup.  Loads are
+// unconditional: an index past the end is clamped to the last block (its
+// result is discarded), so no branch separates a load from its consumer.
+//   amax_bits/namax: values whose max is the tensor amax (fp32 bit patterns):
+//   the amax pass partials, or the caller's amax_in (namax = 1).
+template <bool FOUR_SIX, bool SR, bool RHT>
+__global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, const uint32_t* __restrict__ amax_bits,
+    int namax, float* __restrict__ alpha_out, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, uint8_t* __restrict__ choice, uint32_t seed_lo,
+    uint32_t seed_hi) {
+  __shared__ float2 tab[128];
+  __shared__ float kshared[2];
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t nchunks = (nblocks + kThreads - 1) / kThreads;
+  const int64_t last = nblocks - 1;
+  const int64_t G = gridDim.x;
+  auto blk = [&](int64_t c) {
+    const int64_t b = c * kThreads + threadIdx.x;
+    return b < last ? b : last;
+  };
+
+  int64_t c = blockIdx.x;
+  uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+  if (c < nchunks) {                       // in flight during the prologue
+    const int64_t b = blk(c);
+    a0 = x[2 * b];
+    a1 = x[2 * b + 1];
+  }
+
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < namax; i += kThreads) {
+    const uint32_t a = amax_bits[i];
+    m = m > a ? m : a;
+  }
+  m = block_max_u32(m, red);
+  if (threadIdx.x < 128) {                 // waves 0 and 1: tensor scale and table
+    const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
+    build_scale_table(tab, ts.alpha);
+    if (threadIdx.x == 0) {
+      kshared[0] = ts.k6;
+      kshared[1] = ts.k4;
+      if (blockIdx.x == 0) *alpha_out = ts.alpha;
+    }
+  }
+  __syncthreads();
+  const float k6 = kshared[0], k4 = kshared[1];
+  uint32_t signs = 0;
+  if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
+
+  while (c < nchunks) {
+    const int64_t cb = c + G;
+    {
+      const int64_t b = blk(cb < nchunks ? cb : nchunks - 1);
+      b0 = x[2 * b];
+      b1 = x[2 * b + 1];
+    }
+    {
+      const int64_t b = c * kThreads + threadIdx.x;
+      if (b < nblocks)
+        nvfp4_block<FOUR_SIX, SR, RHT>(a0, a1, b, tab, k6, k4, signs, seed_lo, seed_hi, codes,
+                                       scales, choice);
+    }
+    if (cb >= nchunks) break;
+    const int64_t ca = cb + G;
+    {
+      const int64_t b = blk(ca < nchunks ? ca : nchunks - 1);
+      a0 = x[2 * b];
+      a1 = x[2 * b + 1];
+    }
+    {
+      const int64_t b = cb * kThreads + threadIdx.x;
+      if (b < nblocks)
+        nvfp4_block<FOUR_SIX, SR, RHT>(b0, b1, b, tab, k6, k4, signs, seed_lo, seed_hi, codes,
+                                       scales, choice);
+    }
+    c = ca;
+  }
 }
 
 // ------------------------------------------------------------------ dequantize
