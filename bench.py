@@ -1,20 +1,24 @@
 #!/usr/bin/env python3
-"""Throughput of NVFP4 Four-Over-Six quantization of an 8192x4096 bf16
-activation tensor on one MI355X.
+"""Throughput of block-scaled FP4 quantization on one MI355X.
 
-A step is one full pass of the path over one input: the tensor amax pass
-(Eq. 1) and the block quantizer (Eq. 2-3 with the 4/6 choice), i.e. one
-``nvfp4_quantize`` call with amax computed inside.  Inputs rotate over
-enough resident copies (> 1 GiB together) that no step finds its input in
-the 256 MB last-level cache.
+Headline: NVFP4 Four-Over-Six quantization of an 8192x4096 bf16 activation
+tensor.  A step is one full pass of the path over one input: the tensor amax
+pass (Eq. 1 of "Four Over Six") and the block quantizer (Eq. 2-3 with the
+4/6 choice), i.e. one ``nvfp4_quantize`` call with the amax computed inside.
+Inputs rotate over >= 1 GiB of resident copies, so no step finds its input
+in the 256 MB last-level cache.  Every launch goes through the library's C
+entry points with preallocated buffers, so the GPU, not the host, sets the
+pace.
 
-Reported: effective GB/s over the algorithmic bytes (bf16 read + FP4 codes
-+ E4M3 scales + 4 B tensor scale written), its fraction of the 8 TB/s HBM
-peak, the quantize kernel alone (amax given) timed live with HIP events on
-its stream, optional rocprofv3 traffic for that kernel, and the CPU oracle
-timed on the host as a baseline.
+Reported on one JSON line: effective GB/s over the algorithmic bytes (bf16
+read + FP4 codes + E4M3 scales + 4 B tensor scale), the fraction of the
+8 TB/s HBM peak, the quantize kernel alone (amax given) timed with HIP
+events on its stream, rocprofv3 traffic for that kernel (when the committed
+counter summary matches the current kernel sources), the same figures for
+the other four workloads under "rows", and the CPU oracle timed on the host.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-rows]
+    python bench.py --summarize OUT.md DIR [DIR...]   # rocprofv3 output -> summary
 """
 from __future__ import annotations
 
@@ -29,13 +33,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-ROWS, COLS = 8192, 4096
-WORKLOAD = "nvfp4_four_over_six_8192x4096_bf16"
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_4o6_8192x4096_counters.json")
+
+# workload -> (rows, cols, kind, flags, label)
+ROWS = {
+    "c1": (256, 1024, "nvfp4", 0, "nvfp4_rtn6_256x1024"),
+    "c2": (8192, 4096, "nvfp4", 1, "nvfp4_four_over_six_8192x4096"),
+    "c3": (14336, 4096, "nvfp4", 1 | 8 | 64, "nvfp4_2d16x16_four_over_six_transposed_14336x4096"),
+    "c4": (8192, 14336, "nvfp4", 2 | 4, "nvfp4_rht16_sr_8192x14336"),
+    "c5": (16384, 8192, "mxfp4", 16 | 32 | 64, "mxfp4_had32_row_col_16384x8192"),
+}
+SEED = 0x0123456789ABCDEF
 
 
-def algorithmic_bytes(rows, cols):
+def algorithmic_bytes(wl):
+    rows, cols, kind, flags, _ = ROWS[wl]
     n = rows * cols
+    if kind == "mxfp4":
+        return 2 * n + 2 * (n // 2 + n // 32)
+    if flags & 8:                                    # 16x16 tiles
+        out = n // 2 + n // 256
+        if flags & 64:
+            out *= 2                                 # transposed codes and scales
+        return 2 * n + out + 4
     return 2 * n + n // 2 + n // 16 + 4
 
 
@@ -48,46 +69,243 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(per_launch_alg):
-    """HBM bytes per launch of the quantize kernel from the committed
+def traffic_from_profile():
+    """HBM bytes per launch of the 4/6 quantize kernel from the committed
     rocprofv3 counter summary, or None when it is missing or stale."""
-    path = os.path.join(ROOT, "profiles", "nvfp4_4o6_8192x4096_counters.json")
-    if not os.path.exists(path):
+    if not os.path.exists(COUNTERS_FILE):
         return None
-    with open(path) as f:
+    with open(COUNTERS_FILE) as f:
         p = json.load(f)
     if p.get("kernel_source_sha") != kernel_source_sha():
         return None
     return p.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x_np):
-    """The CPU oracle, as it stands, on the same workload (full tensor,
-    repeated until ~10 s of work); single-threaded."""
+# ------------------------------------------------------------------ GPU side
+class Row:
+    """Preallocated buffers and raw C calls for one workload."""
+
+    def __init__(self, wl, fp4, torch, synthetic, np):
+        self.wl = wl
+        rows, cols, kind, flags, label = ROWS[wl]
+        self.rows, self.cols, self.kind, self.flags, self.label = rows, cols, kind, flags, label
+        dev = torch.device("cuda:0")
+        x_np = synthetic.gen(wl)
+        self.x_np = x_np
+        x0 = torch.from_numpy(x_np.view(np.int16)).to(dev)
+        nbytes = x0.numel() * 2
+        self.nbuf = min(64, max(4, -(-(1 << 30) // nbytes)))   # >= 1 GiB of inputs (c1: 64 copies)
+        self.xs = [x0] + [x0.clone() for _ in range(self.nbuf - 1)]
+        L = fp4.lib()
+        self.L = L
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        u8 = torch.uint8
+        self.outs = []
+        if kind == "nvfp4":
+            two_d = bool(flags & 8)
+            srows = rows // 16 if two_d else rows
+            for _ in range(self.nbuf):
+                o = dict(codes=torch.empty((rows, cols // 2), dtype=u8, device=dev),
+                         scales=torch.empty((srows, cols // 16), dtype=u8, device=dev),
+                         alpha=torch.empty(1, dtype=torch.float32, device=dev),
+                         amax=torch.empty(1, dtype=torch.float32, device=dev))
+                if flags & 64:
+                    o["codes_t"] = torch.empty((cols, rows // 2), dtype=u8, device=dev)
+                    o["scales_t"] = torch.empty((cols // 16, rows // 16), dtype=u8, device=dev)
+                self.outs.append(o)
+            self.ws = torch.empty(max(16, L.fp4_workspace_bytes(rows, cols, flags)), dtype=u8,
+                                  device=dev)
+            for k in range(self.nbuf):          # amax for the kernel-only timing
+                rc = L.fp4_tensor_amax(self.xs[k].data_ptr(), rows, cols, flags, SEED,
+                                       self.outs[k]["amax"].data_ptr(), self.ws.data_ptr(),
+                                       self.ws.numel(), self.sp)
+                assert rc == 0, rc
+        else:
+            for _ in range(self.nbuf):
+                self.outs.append(dict(
+                    codes_r=torch.empty((rows, cols // 2), dtype=u8, device=dev),
+                    scales_r=torch.empty((rows, cols // 32), dtype=u8, device=dev),
+                    codes_c=torch.empty((cols, rows // 2), dtype=u8, device=dev),
+                    scales_c=torch.empty((cols, rows // 32), dtype=u8, device=dev)))
+        # raw pointer tuples, prepared once
+        self.args_step, self.args_kernel = [], []
+        for k in range(self.nbuf):
+            o, xp = self.outs[k], self.xs[k].data_ptr()
+            if kind == "nvfp4":
+                ct = o["codes_t"].data_ptr() if "codes_t" in o else None
+                st = o["scales_t"].data_ptr() if "scales_t" in o else None
+                common = (xp, rows, cols, flags, SEED)
+                tail = (o["alpha"].data_ptr(), o["codes"].data_ptr(), o["scales"].data_ptr(),
+                        None, ct, st)
+                self.args_step.append(common + (None,) + tail +
+                                      (self.ws.data_ptr(), self.ws.numel(), self.sp))
+                self.args_kernel.append(common + (o["amax"].data_ptr(),) + tail +
+                                        (None, 0, self.sp))
+            else:
+                a = (xp, rows, cols, flags, o["codes_r"].data_ptr(), o["scales_r"].data_ptr(),
+                     o["codes_c"].data_ptr(), o["scales_c"].data_ptr(), self.sp)
+                self.args_step.append(a)
+                self.args_kernel.append(a)
+        self.fn = L.nvfp4_quantize if kind == "nvfp4" else L.mxfp4_quantize
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        rc = self.fn(*self.args_step[i % self.nbuf])
+        assert rc == 0, rc
+
+    def kernel(self, i):
+        rc = self.fn(*self.args_kernel[i % self.nbuf])
+        assert rc == 0, rc
+
+
+def time_loop(torch, stream, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_launches(torch, stream, fn, steps, warmup):
+    """Mean duration of single launches: an event pair on the launch stream
+    around every call, so inter-launch gaps are not counted."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def copy_reference(torch, row):
+    """Plain device copy of one input: the achievable bandwidth on this machine."""
+    src, dst = row.xs[1], row.xs[2].clone()
+    ms, _ = time_loop(torch, row.stream, lambda i: dst.copy_(src), 20, 3)
+    return 2 * src.numel() * 2 / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ CPU side
+def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
+    """The CPU oracle, as it stands (single-threaded C), on the workload or
+    on its first max_rows rows; repeated until ~budget_s of work."""
+    import numpy as np
     import oracle
     oracle.build()
+    rows, cols, kind, flags, _ = ROWS[wl]
+    x = x_np if max_rows is None else np.ascontiguousarray(x_np[:max_rows])
     times = []
-    t_end = time.time() + 10.0
-    while time.time() < t_end or len(times) < 2:
+    t_end = time.time() + budget_s
+    while len(times) < 5 and (time.time() < t_end or len(times) < 1):
         t0 = time.perf_counter()
-        oracle.nvfp4_quantize(x_np, oracle.FOUR_OVER_SIX)
+        if kind == "nvfp4":
+            oracle.nvfp4_quantize(x, flags, seed=SEED)
+        else:
+            oracle.mxfp4_quantize(x, flags)
         times.append(time.perf_counter() - t0)
-        if len(times) >= 5:
-            break
     times.sort()
     med = times[len(times) // 2]
-    return {"value": round(algorithmic_bytes(*x_np.shape) / med / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": "full 8192x4096 workload, %d runs, median %.2f s" % (len(times), med)}
+    frac = x.shape[0] / rows
+    gbs = algorithmic_bytes(wl) * frac / med / 1e9
+    what = "full %dx%d workload" % (rows, cols) if max_rows is None else \
+        "first %d of %d rows" % (x.shape[0], rows)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%s, %d runs, median %.2f s" % (what, len(times), med)}
 
 
+# ------------------------------------------------------------------ profile summaries
+def summarize(out_path, dirs, command):
+    """Summarize rocprofv3 output directories (kernel trace and/or --pmc
+    FETCH_SIZE / WRITE_SIZE) into a short markdown file.  Traffic is scaled
+    by what the same counter reads for the plain 64 MiB copy the benchmark
+    runs (its true bytes are known)."""
+    import glob
+    import re
+    import sqlite3
+    import statistics
+
+    def short(n):
+        return re.sub(r"\(.*", "", n).replace("void fp4q::", "").replace("fp4q::", "")
+
+    durations, counters = {}, {}
+    for d in dirs:
+        for db in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            c = sqlite3.connect(db)
+            tabs = {r[0] for r in c.execute("select name from sqlite_master")}
+            if "kernels" in tabs:
+                for n, dur in c.execute("select name, duration from kernels"):
+                    durations.setdefault(short(n), []).append(dur / 1000.0)
+            if "counters_collection" in tabs:
+                for n, cn, v, g in c.execute(
+                        "select kernel_name, counter_name, value, grid_size from counters_collection"):
+                    counters.setdefault((short(n), cn, g), []).append(v)
+    lines = ["# rocprofv3 summary", "", "Command:", "", "```", command, "```", ""]
+    if durations:
+        lines += ["| kernel | launches | avg us | median us | min us | max us |",
+                  "|---|---|---|---|---|---|"]
+        for k, v in sorted(durations.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
+                k, len(v), sum(v) / len(v), statistics.median(v), min(v), max(v)))
+        lines.append("")
+    result = {}
+    if counters:
+        lines += ["| kernel | grid | counter | KiB per dispatch (mean) |", "|---|---|---|---|"]
+        for (k, cn, g), v in sorted(counters.items()):
+            lines.append("| %s | %d | %s | %.1f |" % (k, g, cn, sum(v) / len(v)))
+        copy_bytes = 2 * 8192 * 4096                    # the benchmark's plain copy
+        cal = {}
+        for cn in ("FETCH_SIZE", "WRITE_SIZE"):
+            vs = [sum(v) / len(v) for (k, c2, g), v in counters.items()
+                  if c2 == cn and "copyBuffer" in k]
+            if vs:
+                cal[cn] = copy_bytes / (max(vs) * 1024.0)
+        q = {cn: sum(v) / len(v) for (k, cn, g), v in counters.items()
+             if k.startswith("nvfp4_1d_kernel<true, false, false>")}
+        if cal and q:
+            fetch = q.get("FETCH_SIZE", 0) * 1024 * cal.get("FETCH_SIZE", 1)
+            write = q.get("WRITE_SIZE", 0) * 1024 * cal.get("WRITE_SIZE", 1)
+            lines += ["", "Calibration (plain 64 MiB copy): FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (
+                cal.get("FETCH_SIZE", 0), cal.get("WRITE_SIZE", 0)),
+                "4/6 quantize kernel per launch: fetched %.0f B, written %.0f B, total %.0f B "
+                "(algorithmic %d B)" % (fetch, write, fetch + write, algorithmic_bytes("c2"))]
+            result = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes": round(fetch),
+                      "write_bytes": round(write), "hbm_bytes_per_launch": round(fetch + write),
+                      "algorithmic_bytes": algorithmic_bytes("c2"), "command": command}
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if result:
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(result, f, indent=1)
+    print("\n".join(lines))
+
+
+# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timings")
+    ap.add_argument("--no-rows", action="store_true", help="headline workload only")
+    ap.add_argument("--summarize", nargs="+", metavar=("OUT", "DIR"),
+                    help="summarize rocprofv3 output directories into OUT")
+    ap.add_argument("--command", default="", help="command recorded in a --summarize output")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize[0], args.summarize[1:], args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this quantizer has no multi-GPU path "
               "(sharding needs one all-reduce(max) of the amax; see DESIGN.md)", file=sys.stderr)
@@ -99,71 +317,14 @@ def main():
     import block_scaled_fp4_reduce_amd as fp4
     import synthetic
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    x_np = synthetic.gen("c2")
-    x0 = torch.from_numpy(x_np.view(np.int16)).to(dev)
-    in_bytes = x0.numel() * 2
-    nbuf = max(4, -(-(1 << 30) // in_bytes))            # >= 1 GiB of rotating inputs
-    xs = [x0] + [x0.clone() for _ in range(nbuf - 1)]
-    flags = fp4.FOUR_OVER_SIX
-    outs = [fp4.nvfp4_quantize(x, flags) for x in xs]   # allocates every output once
-    ws = torch.empty(fp4.fp4_workspace_bytes(ROWS, COLS, flags), dtype=torch.uint8, device=dev)
-    amaxes = [fp4.fp4_tensor_amax(x, flags, ws=ws) for x in xs]
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-
-    def step(i):
-        k = i % nbuf
-        fp4.nvfp4_quantize(xs[k], flags, ws=ws, out=outs[k], stream=stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-
-    # dominant kernel alone: quantize with amax given (one kernel per call),
-    # HIP events on the launch stream around every launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i in range(args.warmup):
-        k = i % nbuf
-        fp4.nvfp4_quantize(xs[k], flags, amax=amaxes[k], out=outs[k], stream=stream)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        k = i % nbuf
-        evs[i][0].record(stream)
-        fp4.nvfp4_quantize(xs[k], flags, amax=amaxes[k], out=outs[k], stream=stream)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    kms = sorted(a.elapsed_time(b) for a, b in evs)
-    kernel_ms = sum(kms) / len(kms)
-
-    # plain copy of the same size: the achievable bandwidth on this machine
-    src, dst = xs[1], torch.empty_like(xs[1])
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(20):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * in_bytes * 20 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-
-    alg = algorithmic_bytes(ROWS, COLS)
+    torch.cuda.set_device(0)
+    head = Row("c2", fp4, torch, synthetic, np)
+    ms_step, wall = time_loop(torch, head.stream, head.step, args.steps, args.warmup)
+    ms_kernel = time_launches(torch, head.stream, head.kernel, args.steps, args.warmup)
+    copy_gbs = copy_reference(torch, head)
+    alg = algorithmic_bytes("c2")
     value = alg / (ms_step * 1e-3) / 1e9
-    kernel_gbs = alg / (kernel_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(alg)
+    kernel_gbs = alg / (ms_kernel * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -177,22 +338,39 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "rows": ROWS, "cols": COLS,
+        "config": {"workload": head.label + "_bf16", "rows": 8192, "cols": 4096,
                    "values": "Student-t(4) x per-column lognormal(0,1), bf16",
                    "flags": "FOUR_OVER_SIX", "amax": "computed in-step",
                    "global_batch": 1, "parallelism": "none"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "quantize_kernel": {"ms_avg": round(kernel_ms, 5), "ms_p10": round(kms[len(kms) // 10], 5),
-                            "ms_p90": round(kms[(9 * len(kms)) // 10], 5),
-                            "gbs": round(kernel_gbs, 2)},
+        "quantize_kernel": {"us_avg": round(ms_kernel * 1e3, 3), "gbs": round(kernel_gbs, 2),
+                            "note": "amax given: one kernel per call, event pair per launch"},
         "copy_kernel_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic_from_profile()},
         "wall_s": round(wall, 4),
     }
+    if not args.no_rows:
+        rows = []
+        for wl in ("c1", "c3", "c4", "c5"):
+            r = Row(wl, fp4, torch, synthetic, np)
+            st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
+            kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)
+            a = algorithmic_bytes(wl)
+            entry = {"workload": r.label, "algorithmic_bytes": a,
+                     "step_us": round(st * 1e3, 3), "step_gbs": round(a / (st * 1e-3) / 1e9, 1),
+                     "kernel_us": round(kt * 1e3, 3), "kernel_gbs": round(a / (kt * 1e-3) / 1e9, 1),
+                     "kernel_frac_hbm": round(a / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if not args.no_cpu:
+                entry["cpu_oracle"] = cpu_oracle(wl, r.x_np, max_rows=None if wl == "c1" else 512,
+                                                 budget_s=3.0)
+            rows.append(entry)
+            del r
+            torch.cuda.empty_cache()
+        line["rows"] = rows
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(x_np)
+        line["cpu_baseline"] = cpu_oracle("c2", head.x_np)
     print(json.dumps(line), flush=True)
 
 

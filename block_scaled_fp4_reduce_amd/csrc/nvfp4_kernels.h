@@ -151,7 +151,7 @@ __device__ __forceinline__ float err_pair(uint32_t packed, float s, float y0, fl
 // two fma chains (elements 0..7 and 8..15) that are then added.
 __device__ __forceinline__ float quant16_rtn(const float* y, float s, float r, uint32_t& w0,
                                              uint32_t& w1) {
-  w0 = 0; w1 = 0;
+  // the four byte-wise conversions per word overwrite every byte of w0/w1
   w0 = cvt_fp4x2<0>(w0, y[0] * r, y[1] * r, 1.0f);
   w0 = cvt_fp4x2<1>(w0, y[2] * r, y[3] * r, 1.0f);
   w0 = cvt_fp4x2<2>(w0, y[4] * r, y[5] * r, 1.0f);
@@ -197,8 +197,7 @@ __device__ __forceinline__ float quant16_sr(const float* y, float s, float r, ui
   float q[16];
 #pragma unroll
   for (int i = 0; i < 16; i++) q[i] = sr_value(y[i] * r, idx0 + i, k0, k1);
-  // grid values convert exactly
-  w0 = 0; w1 = 0;
+  // grid values convert exactly; every byte of w0/w1 is overwritten
   w0 = cvt_fp4x2<0>(w0, q[0], q[1], 1.0f);
   w0 = cvt_fp4x2<1>(w0, q[2], q[3], 1.0f);
   w0 = cvt_fp4x2<2>(w0, q[4], q[5], 1.0f);
@@ -228,14 +227,30 @@ __device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t& ca, uint32
 #endif
 }
 
-// Quantize one 16-value block (the lane's) and store codes, scale, choice.
+// Buffer resource over [base, base + bytes): loads past the end read 0 and
+// stores past the end are dropped, so chunk tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// Quantize the lane's 16-value block (raw bf16 in v0, v1) and store codes,
+// scale and choice at byte offsets 8*lane / lane / lane of the chunk's
+// output resources.
 template <bool FOUR_SIX, bool SR, bool RHT>
-__device__ __forceinline__ void nvfp4_block(const uint4& v0, const uint4& v1, int64_t b,
-                                            const float2* tab, float k6, float k4,
-                                            uint32_t signs, uint32_t seed_lo, uint32_t seed_hi,
-                                            uint2* __restrict__ codes,
-                                            uint8_t* __restrict__ scales,
-                                            uint8_t* __restrict__ choice) {
+__device__ __forceinline__ void nvfp4_block(uint4 v0, uint4 v1, int64_t b, const float2* tab,
+                                            float k6, float k4, uint32_t signs, uint32_t seed_lo,
+                                            uint32_t seed_hi, __amdgpu_buffer_rsrc_t rc,
+                                            __amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rh,
+                                            bool want_choice) {
   float y[16];
   unpack8(v0, y);
   unpack8(v1, y + 8);
@@ -254,32 +269,40 @@ __device__ __forceinline__ void nvfp4_block(const uint4& v0, const uint4& v1, in
   uint32_t e6, e4;
   e4m3_pair(amax_b * k6, amax_b * k4, e6, e4);
   const float2 sr6 = tab[e6];
-  uint32_t w0, w1, scale = e6, pick4 = 0;
+  // every byte of the code words is written by the conversions, so they
+  // start from an arbitrary value (no zeroing instruction)
+  uint32_t w0 = __builtin_nondeterministic_value(0u), w1 = __builtin_nondeterministic_value(0u);
+  uint32_t scale = e6, pick4 = 0;
   if constexpr (SR) {
     quant16_sr(y, sr6.x, sr6.y, (uint64_t)b * 16, seed_lo, seed_hi, w0, w1);
   } else {
     const float err6 = quant16_rtn(y, sr6.x, sr6.y, w0, w1);
     if constexpr (FOUR_SIX) {
       const float2 sr4 = tab[e4];
-      uint32_t u0, u1;
+      uint32_t u0 = __builtin_nondeterministic_value(0u), u1 = __builtin_nondeterministic_value(0u);
       const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
-      if (err4 < err6) {  // ties keep M = 6
-        w0 = u0; w1 = u1; scale = e4; pick4 = 1;
-      }
+      pick4 = err4 < err6 ? 1u : 0u;      // ties keep M = 6
+      w0 = pick4 ? u0 : w0;
+      w1 = pick4 ? u1 : w1;
+      scale = pick4 ? e4 : e6;
     }
   }
-  codes[b] = make_uint2(w0, w1);
-  scales[b] = (uint8_t)scale;
-  if (choice) choice[b] = (uint8_t)pick4;
+  const int lane = threadIdx.x;
+  i32x2_t cw;
+  cw.x = (int)w0;
+  cw.y = (int)w1;
+  __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * lane, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)scale, rs, lane, 0, 0);
+  if (want_choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)pick4, rh, lane, 0, 0);
 }
 
 // 1D NVFP4: one lane per 16-value block of the flattened tensor (blocks never
 // straddle rows because cols % 16 == 0).  Persistent workgroups walk chunks
 // of kThreads blocks with a stride of the grid, with two register buffers:
 // chunk i+1 is loaded while chunk i is computed, so memory and VALU work
-// overlap and the tensor-scale prologue runs once per workgroup.  Loads are
-// unconditional: an index past the end is clamped to the last block (its
-// result is discarded), so no branch separates a load from its consumer.
+// overlap and the tensor-scale prologue runs once per workgroup.  All global
+// accesses go through per-chunk buffer resources (uniform base in SGPRs,
+// 32-bit lane offsets, hardware bounds on the last chunk).
 //   amax_bits/namax: values whose max is the tensor amax (fp32 bit patterns):
 //   the amax pass partials, or the caller's amax_in (namax = 1).
 template <bool FOUR_SIX, bool SR, bool RHT>
@@ -291,32 +314,47 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   __shared__ float2 tab[128];
   __shared__ float kshared[2];
   __shared__ uint32_t red[kThreads / 64];
-  const int64_t nchunks = (nblocks + kThreads - 1) / kThreads;
-  const int64_t last = nblocks - 1;
-  const int64_t G = gridDim.x;
-  auto blk = [&](int64_t c) {
-    const int64_t b = c * kThreads + threadIdx.x;
-    return b < last ? b : last;
+  // chunk indices fit in 32 bits (rows*cols < 2^40 -> < 2^28 chunks), which
+  // keeps the per-chunk bookkeeping on the scalar unit
+  const int nchunks = (int)((nblocks + kThreads - 1) / kThreads);
+  const int tail = (int)(nblocks - (int64_t)(nchunks - 1) * kThreads);   // blocks in the last chunk
+  const int G = gridDim.x;
+  const int lane = threadIdx.x;
+  const bool want_choice = choice != nullptr;
+  auto nblk = [&](int cc) { return cc < nchunks - 1 ? kThreads : (cc == nchunks - 1 ? tail : 0); };
+  auto in_rsrc = [&](int cc) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(x + 2 * (int64_t)cc * kThreads), 0,
+                                             nblk(cc) * 32, 0x00020000);
   };
 
-  int64_t c = blockIdx.x;
-  uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-  if (c < nchunks) {                       // in flight during the prologue
-    const int64_t b = blk(c);
-    a0 = x[2 * b];
-    a1 = x[2 * b + 1];
+  // Loads are unconditional: a chunk past the end gets a zero-size resource
+  // and reads zeros without touching memory, so no branch separates a
+  // prefetch from its consumer.
+  int c = blockIdx.x;
+  uint4 a0, a1, b0, b1;
+  {                                        // in flight during the prologue
+    const __amdgpu_buffer_rsrc_t r = in_rsrc(c);
+    a0 = buffer_load16(r, 32 * lane);
+    a1 = buffer_load16(r, 32 * lane + 16);
   }
 
   uint32_t m = 0;
-  for (int i = threadIdx.x; i < namax; i += kThreads) {
-    const uint32_t a = amax_bits[i];
-    m = m > a ? m : a;
+  if ((namax & 3) == 0 && (((uintptr_t)amax_bits) & 15) == 0) {
+    for (int i = lane; 4 * i < namax; i += kThreads) {   // 16-byte loads of the partials
+      const uint4 a = ((const uint4*)amax_bits)[i];
+      m = max(m, max(max(a.x, a.y), max(a.z, a.w)));
+    }
+  } else {
+    for (int i = lane; i < namax; i += kThreads) {
+      const uint32_t a = amax_bits[i];
+      m = m > a ? m : a;
+    }
   }
   m = block_max_u32(m, red);
-  if (threadIdx.x < 128) {                 // waves 0 and 1: tensor scale and table
+  if (lane < 128) {                        // waves 0 and 1: tensor scale and table
     const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
     build_scale_table(tab, ts.alpha);
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
       kshared[0] = ts.k6;
       kshared[1] = ts.k4;
       if (blockIdx.x == 0) *alpha_out = ts.alpha;
@@ -327,32 +365,34 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   uint32_t signs = 0;
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
 
+  auto process = [&](int cc, uint4 v0, uint4 v1) {
+    const int n = nblk(cc);
+    const int64_t b0 = (int64_t)cc * kThreads;
+    nvfp4_block<FOUR_SIX, SR, RHT>(
+        v0, v1, b0 + lane, tab, k6, k4, signs, seed_lo, seed_hi,
+        __builtin_amdgcn_make_buffer_rsrc(codes + b0, 0, n * 8, 0x00020000),
+        __builtin_amdgcn_make_buffer_rsrc(scales + b0, 0, n, 0x00020000),
+        __builtin_amdgcn_make_buffer_rsrc(want_choice ? choice + b0 : scales, 0, want_choice ? n : 0,
+                                          0x00020000),
+        want_choice);
+  };
+
   while (c < nchunks) {
-    const int64_t cb = c + G;
+    const int cb = c + G;
     {
-      const int64_t b = blk(cb < nchunks ? cb : nchunks - 1);
-      b0 = x[2 * b];
-      b1 = x[2 * b + 1];
+      const __amdgpu_buffer_rsrc_t r = in_rsrc(cb);
+      b0 = buffer_load16(r, 32 * lane);
+      b1 = buffer_load16(r, 32 * lane + 16);
     }
-    {
-      const int64_t b = c * kThreads + threadIdx.x;
-      if (b < nblocks)
-        nvfp4_block<FOUR_SIX, SR, RHT>(a0, a1, b, tab, k6, k4, signs, seed_lo, seed_hi, codes,
-                                       scales, choice);
-    }
+    process(c, a0, a1);
     if (cb >= nchunks) break;
-    const int64_t ca = cb + G;
+    const int ca = cb + G;
     {
-      const int64_t b = blk(ca < nchunks ? ca : nchunks - 1);
-      a0 = x[2 * b];
-      a1 = x[2 * b + 1];
+      const __amdgpu_buffer_rsrc_t r = in_rsrc(ca);
+      a0 = buffer_load16(r, 32 * lane);
+      a1 = buffer_load16(r, 32 * lane + 16);
     }
-    {
-      const int64_t b = cb * kThreads + threadIdx.x;
-      if (b < nblocks)
-        nvfp4_block<FOUR_SIX, SR, RHT>(b0, b1, b, tab, k6, k4, signs, seed_lo, seed_hi, codes,
-                                       scales, choice);
-    }
+    process(cb, b0, b1);
     c = ca;
   }
 }

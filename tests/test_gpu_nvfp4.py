@@ -96,6 +96,12 @@ def test_parity_c4_full():
     got, want = run_case(x, fp4.RHT16 | fp4.SR)
 
 
+def test_parity_workloads_at_other_sizes():
+    """Row counts that leave partial chunks for the persistent workgroups."""
+    for rows in (8193, 9000):
+        run_case(S.gen("c2", rows, 4096), fp4.FOUR_OVER_SIX)
+
+
 def test_tensor_amax():
     for flags in (0, fp4.RHT16):
         x = S.gen("c4", 130, 4096)
