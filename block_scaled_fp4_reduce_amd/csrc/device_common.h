@@ -98,6 +98,69 @@ __device__ __forceinline__ void fwht(float* v) {
   }
 }
 
+// ---------------------------------------------------------------- buffer access
+// Buffer resource over [base, base + bytes): loads past the end read 0 and
+// stores past the end are dropped, so tails need no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// ---------------------------------------------------------------- XCD-aware tile order
+// MI355X has 8 XCDs with one L2 each, and consecutive workgroup ids go to
+// consecutive XCDs.  Outputs whose 64-byte segments are completed by
+// neighbouring tiles (scale bytes, transposed codes) must be finished inside
+// one L2, or partial lines reach memory separately.  This maps workgroup ids
+// onto a TY x TX tile grid so that each XCD walks whole SY x SX super-tiles,
+// row-major inside each.  Returns false for ids with no tile (ragged edges).
+#ifndef FP4Q_XCD_ORDER
+#define FP4Q_XCD_ORDER 1
+#endif
+constexpr int kXcds = 8;
+
+struct TileOrder {
+  int64_t ty, tx;
+};
+
+// Tile counts stay below 2^31 (the host caps tensors at 2^40 elements and
+// tiles hold at least 2^10), so the index arithmetic is 32-bit; SY and SX
+// are compile-time powers of two.
+template <int SY, int SX>
+__device__ __forceinline__ bool xcd_tile(uint32_t b, uint32_t TY, uint32_t TX, TileOrder& t) {
+  const uint32_t NSY = (TY + SY - 1) / SY, NSX = (TX + SX - 1) / SX, NS = NSY * NSX;
+  if (!FP4Q_XCD_ORDER || NS < kXcds) {     // too few super-tiles: plain row-major order
+    if (b >= TY * TX) return false;
+    const uint32_t ty = b / TX;
+    t.ty = ty;
+    t.tx = b - ty * TX;
+    return true;
+  }
+  constexpr uint32_t per = (uint32_t)SY * SX;
+  const uint32_t xcd = b % kXcds, k = b / kXcds;
+  const uint32_t s = (k / per) * kXcds + xcd, within = k % per;
+  if (s >= NS) return false;
+  const uint32_t sy = s / NSX, sx = s - sy * NSX;
+  const uint32_t ty = sy * SY + within / SX, tx = sx * SX + within % SX;
+  t.ty = ty;
+  t.tx = tx;
+  return ty < TY && tx < TX;
+}
+
+// Grid size for xcd_tile over a TY x TX tile grid.
+__host__ __device__ inline int64_t xcd_grid(int64_t TY, int64_t TX, int SY, int SX) {
+  const int64_t NSY = (TY + SY - 1) / SY, NSX = (TX + SX - 1) / SX, NS = NSY * NSX;
+  if (!FP4Q_XCD_ORDER || NS < kXcds) return TY * TX;
+  return ((NS + kXcds - 1) / kXcds) * kXcds * (int64_t)SY * SX;
+}
+
 // ---------------------------------------------------------------- wave/workgroup max
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 #pragma unroll

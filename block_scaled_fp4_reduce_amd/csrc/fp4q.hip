@@ -154,7 +154,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   if (two_d) {
     const bool f46 = (flags & FP4_FOUR_OVER_SIX) != 0;
     launch_nvfp4_2d(x, rows, cols, f46, abits, namax, alpha_out, codes, scales, choice,
-                    want_t ? codes_t : nullptr, want_t ? scales_t : nullptr, st);
+                    want_t ? codes_t : nullptr, want_t ? scales_t : nullptr, st, num_cus());
     return launched();
   }
   const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
@@ -189,7 +189,7 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   if (n == 0) return FP4_OK;
   launch_mxfp4(x, rows, cols, (flags & FP4_HAD32) != 0, rw ? codes_r : nullptr,
                rw ? scales_r : nullptr, cw ? codes_c : nullptr, cw ? scales_c : nullptr,
-               (hipStream_t)stream);
+               (hipStream_t)stream, num_cus());
   return launched();
 }
 

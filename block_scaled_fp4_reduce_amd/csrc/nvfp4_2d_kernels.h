@@ -14,7 +14,11 @@
 // whose result is bit-identical in every lane.  The transposed codes are
 // recomputed from an LDS copy of the tile with the same scale, so they are
 // the same fp32 operations on the same values and equal the row-wise codes
-// by construction.
+// by construction.  Workgroups are persistent (the next 64x256 tile is
+// loaded while the current one is computed) and take tiles in XCD-aware
+// order (16x4 tiles per XCD super-tile, grid a multiple of 8) so the
+// transposed codes and the scale bytes that neighbouring tiles write into
+// one 64-byte segment are completed in the same L2.
 #pragma once
 
 #include "device_common.h"
@@ -24,25 +28,51 @@ namespace fp4q {
 
 constexpr bool kHave2D = true;
 constexpr int k2dStrips = 4;                 // 64-column strips per workgroup
+constexpr int k2dSuperY = 16, k2dSuperX = 4; // workgroups per XCD super-tile (1024x1024 values)
 constexpr int k2dTileLds = 16 * 16 + 16;     // bf16 per tile in LDS (+32 B pad: no bank conflicts)
+#ifndef FP4Q_2D_WG_PER_CU
+#define FP4Q_2D_WG_PER_CU 2
+#endif
+constexpr int k2dWgPerCu = FP4Q_2D_WG_PER_CU; // persistent workgroups per CU
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) {
-  return __int_as_float(__shfl_xor(__float_as_int(v), m, 16));
+struct Strips {   // one lane's tile row in each of the k2dStrips strips
+  uint4 v[2 * k2dStrips];
+};
+
+// Cross-lane reads inside a 16-lane DPP row (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
 
-// Max / sum over the 16 lanes of a tile, same bits in every lane.
+// Max / sum over the 16 lanes of a tile, same bits in every lane.  After
+// the xor-1 and xor-2 steps every group of 4 lanes holds one value, after
+// the half-row mirror every group of 8, so the mirrors pair exactly the
+// groups an xor-4 / xor-8 butterfly would: the sum is the pairwise tree
+// ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) + (same for 8..15).
 __device__ __forceinline__ float tile_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 1));
-  v = fmaxf(v, shfl_xor_f(v, 2));
-  v = fmaxf(v, shfl_xor_f(v, 4));
-  return fmaxf(v, shfl_xor_f(v, 8));
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
 }
 
 __device__ __forceinline__ float tile_sum(float v) {
-  v = v + shfl_xor_f(v, 1);
-  v = v + shfl_xor_f(v, 2);
-  v = v + shfl_xor_f(v, 4);
-  return v + shfl_xor_f(v, 8);
+  v = v + dpp_f<kDppXor1>(v);
+  v = v + dpp_f<kDppXor2>(v);
+  v = v + dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+
+// Order LDS traffic of one wave (its lanes exchange data through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <bool FOUR_SIX, bool TRANSPOSE>
@@ -58,11 +88,9 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = lane >> 4, r = lane & 15;                 // tile in wave, row in tile
   const int64_t bcols = cols / 16, brows = rows / 16;
-  const int64_t tiles_x = (bcols + 4 * k2dStrips - 1) / (4 * k2dStrips);
-  const int64_t wg_y = blockIdx.x / tiles_x, wg_x = blockIdx.x - wg_y * tiles_x;
-  const int64_t br = wg_y * 4 + wave;                        // tile row of this wave
-  const bool row_ok = br < brows;
-  const int64_t row = br * 16 + r;
+  const uint32_t TY = (uint32_t)((brows + 3) / 4);
+  const uint32_t TX = (uint32_t)((bcols + 4 * k2dStrips - 1) / (4 * k2dStrips));
+  const uint32_t nslots = (uint32_t)xcd_grid(TY, TX, k2dSuperY, k2dSuperX);
 
   uint32_t m = 0;
   for (int i = threadIdx.x; i < namax; i += kThreads) {
@@ -74,78 +102,121 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   if (blockIdx.x == 0 && threadIdx.x == 0) *alpha_out = ts.alpha;
   build_scale_table(tab, ts.alpha);
   __syncthreads();
+  if (nslots == 0) return;                   // empty tensor: only the tensor scale
 
   uint16_t* st = stage[wave][tile];
-  for (int s = 0; s < k2dStrips; s++) {
-    const int64_t bc = (wg_x * k2dStrips + s) * 4 + tile;   // tile column
-    const bool ok = row_ok && bc < bcols;
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (ok) {
-      const uint4* src = (const uint4*)(x + row * cols + bc * 16);
-      v0 = src[0];
-      v1 = src[1];
-    }
-    float y[16];
-    unpack8(v0, y);
-    unpack8(v1, y + 8);
-    float amax_r = 0.0f;
+  // Decode `slot` and load this lane's row of its 4 strips.  Every load is
+  // issued (addresses clamped into the tensor) so the compiler keeps the
+  // next workgroup tile's loads in flight while this one is computed;
+  // values of positions outside the tensor are never stored.
+  auto load = [&](uint32_t slot, Strips& in, TileOrder& to) {
+    const bool valid = slot < nslots && xcd_tile<k2dSuperY, k2dSuperX>(slot, TY, TX, to);
+    if (!valid) to.ty = to.tx = -1;
+    const int64_t row = valid ? (to.ty * 4 + wave) * 16 + r : 0;
+    const int64_t rr = row < rows ? row : rows - 1;
+    const int64_t bc0 = valid ? to.tx * k2dStrips * 4 + tile : 0;
 #pragma unroll
-    for (int k = 0; k < 16; k++) amax_r = fmaxf(amax_r, fabsf(y[k]));
-    const float amax_b = tile_max(amax_r);
+    for (int s = 0; s < k2dStrips; s++) {
+      int64_t bc = bc0 + 4 * s;
+      bc = bc < bcols ? bc : bcols - 1;
+      const uint4* src = (const uint4*)(x + rr * cols + bc * 16);
+      in.v[2 * s] = src[0];
+      in.v[2 * s + 1] = src[1];
+    }
+  };
 
-    const uint32_t e6 = e4m3_rne(amax_b * ts.k6);
-    float2 sr = tab[e6];
-    uint32_t w0, w1, scale = e6, pick4 = 0;
-    const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
-    if constexpr (FOUR_SIX) {
-      const uint32_t e4 = e4m3_rne(amax_b * ts.k4);
-      const float2 sr4 = tab[e4];
-      uint32_t u0, u1;
-      const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
-      if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
-        w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
-      }
-    }
-    if (ok) {
-      *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
-      if (r == 0) {
-        scales[br * bcols + bc] = (uint8_t)scale;
-        if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
-        if constexpr (TRANSPOSE) scales_t[bc * brows + br] = (uint8_t)scale;
-      }
-    }
-    if constexpr (TRANSPOSE) {
-      // stage the tile (bf16, row r at st[16 r]), then lane r takes column r
-      *(uint4*)(st + 16 * r) = v0;
-      *(uint4*)(st + 16 * r + 8) = v1;
-      __syncthreads();
-      float yc[16];
+  Strips cur, nxt;
+  TileOrder tcur, tnxt;
+  uint32_t slot = blockIdx.x;
+  load(slot, cur, tcur);
+  while (slot < nslots) {
+    const uint32_t next = slot + gridDim.x;  // grid is a multiple of 8: same XCD
+    load(next, nxt, tnxt);
+    if (tcur.ty >= 0) {                      // uniform over the workgroup
+      const int64_t br = tcur.ty * 4 + wave;                 // tile row of this wave
+      const bool row_ok = br < brows;
+      const int64_t row = br * 16 + r;
 #pragma unroll
-      for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
-      const float rr = sr.y;
-      uint32_t t0 = 0, t1 = 0;
-      t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
-      t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
-      t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
-      t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
-      t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
-      t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
-      t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
-      t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
-      if (ok) *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
-      __syncthreads();
+      for (int s = 0; s < k2dStrips; s++) {
+        const int64_t bc = (tcur.tx * k2dStrips + s) * 4 + tile;   // tile column
+        const bool ok = row_ok && bc < bcols;
+        const uint4 v0 = cur.v[2 * s], v1 = cur.v[2 * s + 1];
+        float y[16];
+        unpack8(v0, y);
+        unpack8(v1, y + 8);
+        float amax_r = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; k++) amax_r = fmaxf(amax_r, fabsf(y[k]));
+        const float amax_b = tile_max(amax_r);
+
+        uint32_t e6, e4;
+        e4m3_pair(amax_b * ts.k6, amax_b * ts.k4, e6, e4);
+        float2 sr = tab[e6];
+        uint32_t w0, w1, scale = e6, pick4 = 0;
+        const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
+        if constexpr (FOUR_SIX) {
+          const float2 sr4 = tab[e4];
+          uint32_t u0, u1;
+          const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
+          if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
+            w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
+          }
+        }
+        if (ok) {
+          *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
+          if (r == 0) {
+            scales[br * bcols + bc] = (uint8_t)scale;
+            if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
+          }
+        }
+        if constexpr (TRANSPOSE) {
+          // stage the tile (bf16, row r at st[16 r]), then lane r takes column r;
+          // each wave uses its own LDS slots, so a wave-level sync suffices
+          *(uint4*)(st + 16 * r) = v0;
+          *(uint4*)(st + 16 * r + 8) = v1;
+          wave_lds_sync();
+          float yc[16];
+#pragma unroll
+          for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
+          const float rr = sr.y;
+          uint32_t t0 = 0, t1 = 0;
+          t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
+          t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
+          t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
+          t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
+          t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
+          t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
+          t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
+          t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
+          if (ok) {
+            // column 16*tile + r, tile row br: 8 bytes; the 4 waves and the
+            // workgroup below (same XCD) complete the column's 64-byte segment
+            *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
+            if (r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
+          }
+          wave_lds_sync();                   // reads done before the next strip's writes
+        }
+      }
     }
+    cur = nxt;
+    tcur = tnxt;
+    slot = next;
   }
 }
 
 inline void launch_nvfp4_2d(const uint16_t* x, int64_t rows, int64_t cols, bool f46,
                             const uint32_t* abits, int namax, float* alpha_out, uint8_t* codes,
                             uint8_t* scales, uint8_t* choice, uint8_t* codes_t,
-                            uint8_t* scales_t, hipStream_t st) {
+                            uint8_t* scales_t, hipStream_t st, int num_cus) {
   const int64_t bcols = cols / 16, brows = rows / 16;
   const int64_t tiles_x = (bcols + 4 * k2dStrips - 1) / (4 * k2dStrips);
   const int64_t tiles_y = (brows + 3) / 4;
-  int64_t grid = tiles_x * tiles_y;
+  const int64_t nslots = xcd_grid(tiles_y, tiles_x, k2dSuperY, k2dSuperX);
+  // persistent: a multiple of 8 workgroups (XCD count); at least one, so
+  // the tensor scale is written even for an empty tensor
+  int64_t grid = (int64_t)num_cus * k2dWgPerCu;
+  if (grid > nslots) grid = nslots;
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid < 1) grid = 1;
   const bool tr = codes_t != nullptr;
 #define FP4Q_2D(F, T)                                                                   \

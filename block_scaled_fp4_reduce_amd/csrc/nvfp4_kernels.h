@@ -50,35 +50,53 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
     const uint4* __restrict__ x, int64_t ngroups16, uint32_t* __restrict__ partials,
     uint32_t seed_lo, uint32_t seed_hi) {
   __shared__ uint32_t red[kAmaxThreads / 64];
-  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-  int64_t g = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   uint32_t m = 0;
   if constexpr (!RHT) {
-    // magnitude bits of two bf16 per dword; packed 16-bit integer max
+    // Magnitude bits of two bf16 per dword; packed 16-bit integer max.
+    // Workgroups walk chunks of kAmaxThreads * kAmaxUnroll 16-byte vectors
+    // with a stride of the grid; a buffer resource per chunk makes loads
+    // past the end read 0, so every load is issued unconditionally and the
+    // next chunk is in flight while this one is reduced.
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    u16x2 mm = {0, 0};
+    constexpr int64_t CH = (int64_t)kAmaxThreads * kAmaxUnroll;
     const int64_t nvec = ngroups16 * 2;            // 8 bf16 per uint4
-    for (int64_t i = g; i < nvec; i += stride * kAmaxUnroll) {
+    const int64_t nch = (nvec + CH - 1) / CH;
+    auto rsrc = [&](int64_t c) {
+      const int64_t left = c < nch ? nvec - c * CH : 0;
+      return buffer_rsrc(x + (c < nch ? c : 0) * CH, (left < CH ? left : CH) * 16);
+    };
+    struct Chunk {
       uint4 v[kAmaxUnroll];
+    };
+    auto load = [&](int64_t c, Chunk& k) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(c);
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; u++)
+        k.v[u] = buffer_load16(r, (u * kAmaxThreads + (int)threadIdx.x) * 16);
+    };
+    u16x2 mm = {0, 0};
+    Chunk cur, nxt;
+    int64_t c = blockIdx.x;
+    load(c, cur);
+    for (; c < nch; c += gridDim.x) {
+      load(c + gridDim.x, nxt);
 #pragma unroll
       for (int u = 0; u < kAmaxUnroll; u++) {
-        const int64_t j = i + u * stride;
-        v[u] = j < nvec ? x[j] : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; u++) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const uint32_t w[4] = {cur.v[u].x, cur.v[u].y, cur.v[u].z, cur.v[u].w};
 #pragma unroll
         for (int k = 0; k < 4; k++) {
           const uint32_t a = w[k] & 0x7FFF7FFFu;
           mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, a));
         }
       }
+      cur = nxt;
     }
     const uint32_t lo = mm.x, hi = mm.y;
     m = (lo > hi ? lo : hi) << 16;
   } else {
     const uint32_t signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    const int64_t g = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
     float fm = 0.0f;
     for (int64_t i = g; i < ngroups16; i += stride) {
       const uint4 v0 = x[2 * i], v1 = x[2 * i + 1];
@@ -225,21 +243,6 @@ __device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t& ca, uint32
   ca = e4m3_rne(a);
   cb = e4m3_rne(b);
 #endif
-}
-
-// Buffer resource over [base, base + bytes): loads past the end read 0 and
-// stores past the end are dropped, so chunk tails need no branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
-}
-
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
 }
 
 // Quantize the lane's 16-value block (raw bf16 in v0, v1) and store codes,
