@@ -5,6 +5,8 @@
 // (bias 7, max 448); UE8M0 power-of-two scales for MXFP4.
 #pragma once
 
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,6 +98,18 @@ __device__ __forceinline__ void fwht(float* v) {
       v[j + h] = a - b;
     }
   }
+}
+
+// ---------------------------------------------------------------- compile-time loops
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>): register
+// arrays indexed inside stay in registers whatever the unroller decides.
+template <typename F, int... K>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ---------------------------------------------------------------- buffer access

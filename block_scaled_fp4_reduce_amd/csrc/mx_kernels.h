@@ -6,19 +6,37 @@
 // (a fixed, deterministic Hadamard rotation before quantizing, for both
 // operands of the weight-gradient product, hence both orientations).
 //
-// Mapping onto the chip: a workgroup of 4*kMxRows threads owns one
-// kMxRows x 128 tile at a time.  Each thread loads one 32-value row group
-// (four 16-byte loads), quantizes it row-wise straight from registers, and
-// stores it to LDS; after one barrier each thread reads one 32-value column
-// group back from LDS (a wave reads 64 adjacent columns of one row per
-// instruction: 128 contiguous bytes, no bank conflicts) and quantizes it
-// column-wise.  Row pitch in LDS is padded by 16 bytes so the row-group
-// stores do not collide on banks.  Workgroups are persistent and load the
-// next tile while computing the current one.  Tiles are handed out in
-// XCD-aware order (16x16-tile super-tiles per XCD; the grid is a multiple
-// of 8 so a workgroup's tiles stay on its XCD), so the scale bytes that
-// neighbouring tiles write into one 64-byte segment all land in the same L2
-// before the line goes to memory.
+// Mapping onto the chip.  A workgroup of 8 waves owns one 128x128 tile at a
+// time, staged through LDS in three steps, so every global access is a
+// full, coalesced segment (the kernel is bound by the memory pipeline, not
+// by arithmetic, once the rotation runs on the matrix cores):
+//  1. the tile is read with 16-byte non-temporal loads, 16 lanes per
+//     256-byte row piece, and written to LDS (the next tile's loads are
+//     already in flight);
+//  2. each wave quantizes two 32x32 blocks row-wise and two column-wise,
+//     staging codes and scales in LDS;
+//  3. codes leave as 16-byte stores, four lanes per 64-byte row (or
+//     column) segment, and scales as bytes, four per row (or column).
+// With the rotation, the 32-point transforms are dense 32x32 products (the
+// Hadamard matrix H, entries +-1, exact in bf16) on the matrix cores:
+// v_mfma_f32_32x32x16_bf16 twice per 32x32 block, products exact and sums
+// accumulated in fp32 in the hardware's order (rotated values may differ
+// from a butterfly's in the last bits: the accepted tolerance for rotated
+// paths).  Without it, each lane reads its values straight from LDS in the
+// same layout, and the results are exact.
+//
+// Instruction layout (lane l, element j = 0..7; verified on the device):
+//   A[m][k]: m = l % 32, k = 8*(l/32) + j      B[k][n]: k = 8*(l/32) + j, n = l % 32
+//   D[m][n] (16 fp32): n = l % 32, m = 8*(i/4) + 4*(l/32) + i%4, i = 0..15
+// Both orientations are D = H * B, so a 32-value group is column n of D and
+// lies in lanes n and n + 32 (16 values each):
+//   row-wise:    B[k][n] = X[row n][col k]      column-wise: B[k][n] = X[row k][col n]
+// Lanes l < 32 ("A") hold group elements {0-3, 8-11, 16-19, 24-27}, lanes
+// l >= 32 ("B") {4-7, 12-15, 20-23, 28-31}; one lane swap
+// (v_permlane32_swap) shares the group maximum and regroups the codes so
+// that lane A holds bytes 0-7 and lane B bytes 8-15 of the group's 16 code
+// bytes.  Tiles go to workgroups in XCD-aware order (16x16-tile super-tiles
+// per XCD, grid a multiple of 8), so partial segments meet in one L2.
 #pragma once
 
 #include "device_common.h"
@@ -26,165 +44,275 @@
 namespace fp4q {
 
 constexpr bool kHaveMx = true;
-#ifndef FP4Q_MX_ROWS
-#define FP4Q_MX_ROWS 128
-#endif
-constexpr int kMxTile = 128;                     // tile columns
-constexpr int kMxRows = FP4Q_MX_ROWS;            // tile rows (64 or 128)
-constexpr int kMxThreads = kMxRows * 4;          // one row group and one column group per thread
-constexpr int kMxPitch = kMxTile + 8;            // bf16 per LDS row (16-byte pad)
 #ifndef FP4Q_MX_WG_PER_CU
 #define FP4Q_MX_WG_PER_CU 2
 #endif
-constexpr int kMxWgPerCu = FP4Q_MX_WG_PER_CU;    // persistent workgroups per CU
+constexpr int kMxThreads = 512;                  // 8 waves
+constexpr int kMxTile = 128;                     // tile rows and columns
+constexpr int kMxPitch = kMxTile + 8;            // bf16 per LDS row of the input tile
+constexpr int kMxCodePitch = 80;                 // bytes per LDS row of a code stage (64 + pad)
+constexpr int kMxSuper = 16;                     // 16x16 tiles per XCD super-tile
+constexpr int kMxWgPerCu = FP4Q_MX_WG_PER_CU;    // persistent workgroups per CU (LDS: 55 KiB each)
 
 // fp32 nearest to 1/sqrt(32) (bit pattern 0x3E3504F3): orthonormal H32.
 constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
 
-// Quantize 32 values (already rotated if asked) to MXFP4: UE8M0 code of
-// floor(log2 amax) - 2 (0 for zero or subnormal maxima), then nearest-even
-// E2M1 of y / 2^e, done by the hardware conversion with the power-of-two
-// scale in its exponent operand.  Returns the scale code; codes in w[0..3].
-__device__ __forceinline__ uint32_t mx_quant32(float* y, uint32_t* w) {
-  float amax = 0.0f;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // plain vector: stays in VGPRs
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// H[l % 32][16 h + 8 (l/32) + j] as bf16 +-1 (entries (-1)^popcount(m & k)).
+__device__ __forceinline__ bf16x8_t had32_operand(int lane, int h) {
+  uint32_t w[4];
 #pragma unroll
-  for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(y[k]));
-  const int ef = (int)(__float_as_uint(amax) >> 23);           // biased exponent of amax
-  const uint32_t code = (uint32_t)(ef > 2 ? ef - 2 : 0);        // e + 127, e >= -127
-  float scale = __uint_as_float(code << 23);                    // 2^e (exponent field = code)
-  if (code == 0) {
-    // e = -127: scale the (tiny) values by 2^127 exactly first and convert
-    // with unit scale, so the conversion never sees a zero exponent field
-#pragma unroll
-    for (int k = 0; k < 32; k++) y[k] = y[k] * 0x1p127f;
-    scale = 1.0f;
-  }
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
+  for (int p = 0; p < 4; p++) {
     uint32_t v = 0;
-    v = cvt_fp4x2<0>(v, y[8 * d + 0], y[8 * d + 1], scale);
-    v = cvt_fp4x2<1>(v, y[8 * d + 2], y[8 * d + 3], scale);
-    v = cvt_fp4x2<2>(v, y[8 * d + 4], y[8 * d + 5], scale);
-    v = cvt_fp4x2<3>(v, y[8 * d + 6], y[8 * d + 7], scale);
-    w[d] = v;
-  }
-  return code;
-}
-
-template <bool HAD>
-__device__ __forceinline__ void mx_rotate(float* y) {
-  if constexpr (HAD) {
-    fwht<32>(y);
 #pragma unroll
-    for (int k = 0; k < 32; k++) y[k] = y[k] * kInvSqrt32;
+    for (int q = 0; q < 2; q++) {
+      const int k = 16 * h + 8 * (lane >> 5) + 2 * p + q, m = lane & 31;
+      v |= (uint32_t)((__builtin_popcount(m & k) & 1) ? 0xBF80u : 0x3F80u) << (16 * q);
+    }
+    w[p] = v;
   }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-constexpr int kMxSuper = 16;
+// v_permlane32_swap(X, Y) leaves X' = (X[0..31], Y[0..31]) and
+// Y' = (X[32..63], Y[32..63]) across the two half-waves: with X = Y = v,
+// every lane then holds its own value and its partner's (lane l ^ 32).
 
-struct Group32 {   // one thread's 32 bf16 values of a tile row (four 16-byte pieces)
-  uint4 a, b, c, d;
-};   // 16x16 tiles (2048x2048 values) per XCD super-tile
+// Quantize one 32-value group held as 16 + 16 values by a lane pair (this
+// lane's y[i] is group element 8*(i/4) + 4*(lane/32) + i%4): exponent
+// e = floor(log2 amax) - 2 (UE8M0 code e + 127, 0 for zero or subnormal
+// maxima), then nearest-even E2M1 of y / 2^e by the hardware conversion with
+// the power-of-two scale in its exponent operand.  Returns the 8 code bytes
+// this lane stores (lo, hi) and the scale code.
+__device__ __forceinline__ void mx_quant_pair(const float* y, uint32_t& lo, uint32_t& hi,
+                                              uint32_t& code) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) am = fmaxf(am, fabsf(y[i]));
+  const auto m2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(am), __float_as_uint(am),
+                                                   false, false);
+  am = fmaxf(__uint_as_float(m2[0]), __uint_as_float(m2[1]));   // own and partner maximum
+  const int ef = (int)(__float_as_uint(am) >> 23);              // biased exponent of amax
+  code = (uint32_t)(ef > 2 ? ef - 2 : 0);
+  // 2^e with exponent field = code; the conversion reads a zero field as
+  // 2^-127 (checked on the device over every |y| < 2^-121), so tiny groups
+  // need no special case
+  const float scale = __uint_as_float(code << 23);
+  uint32_t d01 = __builtin_nondeterministic_value(0u), d23 = __builtin_nondeterministic_value(0u);
+  d01 = cvt_fp4x2<0>(d01, y[0], y[1], scale);     // elements 8q + 4 (l/32) + 0..3, q = 0
+  d01 = cvt_fp4x2<1>(d01, y[2], y[3], scale);
+  d01 = cvt_fp4x2<2>(d01, y[4], y[5], scale);     // q = 1
+  d01 = cvt_fp4x2<3>(d01, y[6], y[7], scale);
+  d23 = cvt_fp4x2<0>(d23, y[8], y[9], scale);     // q = 2
+  d23 = cvt_fp4x2<1>(d23, y[10], y[11], scale);
+  d23 = cvt_fp4x2<2>(d23, y[12], y[13], scale);   // q = 3
+  d23 = cvt_fp4x2<3>(d23, y[14], y[15], scale);
+  // code word q = A.half_q | B.half_q << 16; lane A stores words 0, 1 and
+  // lane B words 2, 3.  One swap of (d01, d23) hands lane A (d01_A, d01_B)
+  // and lane B (d23_A, d23_B): the A and B halves of the words it stores.
+  const auto r = __builtin_amdgcn_permlane32_swap(d01, d23, false, false);
+  const uint32_t a = r[0], b = r[1];
+  lo = (a & 0xFFFFu) | (b << 16);
+  hi = (a >> 16) | (b & 0xFFFF0000u);
+}
+
+struct Tile4 {      // one thread's four 16-byte pieces of a tile (separate members:
+  u32x4_t v0, v1, v2, v3;   // never an indexed array)
+  template <int P>
+  __device__ __forceinline__ u32x4_t& at() {
+    static_assert(P >= 0 && P < 4, "piece index");
+    if constexpr (P == 0) return v0;
+    else if constexpr (P == 1) return v1;
+    else if constexpr (P == 2) return v2;
+    else return v3;
+  }
+};
 
 template <bool HAD, bool ROW, bool COL>
 __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ codes_r,
     uint8_t* __restrict__ scales_r, uint8_t* __restrict__ codes_c,
     uint8_t* __restrict__ scales_c) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kMxRows * kMxPitch];
-  const int t = threadIdx.x;
-  const int r = t >> 2, g = t & 3;                 // row group of this thread
-  const uint32_t TY = (uint32_t)((rows + kMxRows - 1) / kMxRows);
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kMxTile * kMxPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t rcode[ROW ? kMxTile * kMxCodePitch : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ccode[COL ? kMxTile * kMxCodePitch : 16];
+  __shared__ uint8_t rscale[ROW ? kMxTile * 4 : 4];
+  __shared__ uint8_t cscale[COL ? kMxTile * 4 : 4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  const bool is_a = half == 0;
+  const uint32_t TY = (uint32_t)((rows + kMxTile - 1) / kMxTile);
   const uint32_t TX = (uint32_t)((cols + kMxTile - 1) / kMxTile);
-  constexpr int SY = kMxSuper * (kMxTile / kMxRows), SX = kMxSuper;
-  const uint32_t nslots = (uint32_t)xcd_grid(TY, TX, SY, SX);
+  const uint32_t nslots = (uint32_t)xcd_grid(TY, TX, kMxSuper, kMxSuper);
+  bf16x8_t h0 = {}, h1 = {};
+  if constexpr (HAD) {
+    h0 = had32_operand(lane, 0);
+    h1 = had32_operand(lane, 1);
+  }
 
-  // Decode `slot` and load this thread's row group of its tile.  Every load
-  // is issued (addresses clamped into the tensor) so the compiler can keep
-  // the next tile's loads in flight; values loaded for positions outside
-  // the tensor are never stored (row groups need col < cols, column groups
-  // row < rows, and cols % 8 == 0 keeps each 16-byte piece inside a row).
-  auto load = [&](uint32_t slot, Group32& v, TileOrder& to) {
-    const bool valid = slot < nslots && xcd_tile<SY, SX>(slot, TY, TX, to);
+  // Piece p = t + 512 P of the tile: row p / 16 = t / 16 + 32 P, columns
+  // 8 (t % 16) .. +7.  Pieces outside the tensor read x[0..7] instead
+  // (cols % 8 == 0 keeps a piece inside its row); their values are never
+  // stored.  Offsets within a tile are per-thread constants.
+  const int lr = t >> 4, lc = 8 * (t & 15);
+  const int64_t ld_off = (int64_t)lr * cols + lc;
+  auto load = [&](uint32_t slot, Tile4& v, TileOrder& to) {
+    const bool valid = slot < nslots && xcd_tile<kMxSuper, kMxSuper>(slot, TY, TX, to);
     if (!valid) to.ty = to.tx = -1;
-    const int64_t row = valid ? to.ty * kMxRows + r : 0;
-    const int64_t rr = row < rows ? row : rows - 1;
-    const int64_t c0 = valid ? to.tx * kMxTile + 32 * g : 0;
-    const uint16_t* src = x + rr * cols;
-    auto piece = [&](int j) {
-      const int64_t c = c0 + 8 * j < cols ? c0 + 8 * j : cols - 8;
-      return *(const uint4*)(src + c);
-    };
-    v.a = piece(0);
-    v.b = piece(1);
-    v.c = piece(2);
-    v.d = piece(3);
+    const int64_t R0 = valid ? to.ty * kMxTile : 0, C0 = valid ? to.tx * kMxTile : 0;
+    const uint16_t* base = x + R0 * cols + C0 + ld_off;
+    // rows / columns left from the tile origin, capped to 32 bits (uniform)
+    const int rem_r = valid ? (int)(rows - R0 < kMxTile ? rows - R0 : kMxTile) : 0;
+    const int rem_c = valid ? (int)(cols - C0 < kMxTile ? cols - C0 : kMxTile) : 0;
+    const bool col_ok = lc < rem_c;
+    static_for<4>([&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      const bool ok = col_ok && lr + 32 * P < rem_r;
+      // non-temporal: the input is read once, so it should not displace the
+      // partially written code lines that L2 is combining
+      v.template at<P>() =
+          __builtin_nontemporal_load((const u32x4_t*)(ok ? base + (int64_t)32 * P * cols : x));
+    });
   };
 
-  Group32 cur, nxt;
-  TileOrder tcur, tnxt;
-  uint32_t slot = blockIdx.x;
-  load(slot, cur, tcur);
-  while (slot < nslots) {
-    const uint32_t next = slot + gridDim.x;    // grid is a multiple of 8: same XCD
-    load(next, nxt, tnxt);                     // in flight while this tile is computed
-    const TileOrder to = tcur;
-    if (to.ty >= 0) {                          // uniform over the workgroup
-      const int64_t R0 = to.ty * kMxRows, C0 = to.tx * kMxTile;
-      const int64_t row = R0 + r, c0 = C0 + 32 * g;
-      if constexpr (COL) {
-        uint4* dst = (uint4*)(tile + r * kMxPitch + 32 * g);
-        dst[0] = cur.a;
-        dst[1] = cur.b;
-        dst[2] = cur.c;
-        dst[3] = cur.d;
-      }
-      if constexpr (ROW) {
-        if (row < rows && c0 < cols) {         // cols % 32 == 0: the group is whole
-          float y[32];
-          unpack8(cur.a, y);
-          unpack8(cur.b, y + 8);
-          unpack8(cur.c, y + 16);
-          unpack8(cur.d, y + 24);
-          mx_rotate<HAD>(y);
-          uint32_t w[4];
-          const uint32_t code = mx_quant32(y, w);
-          // lanes 4r..4r+3 store one row's 64 contiguous bytes in one instruction
-          *(uint4*)(codes_r + row * (cols / 2) + c0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
-          scales_r[row * (cols / 32) + c0 / 32] = (uint8_t)code;
-        }
-      }
-      if constexpr (COL) {
-        __syncthreads();
-        // column groups: thread t takes tile column t%128, rows 32*(t/128) .. +31;
-        // a column's pieces come from the kMxRows/32 groups of this workgroup
-        const int c = t & (kMxTile - 1), gc = t >> 7;
-        const int64_t col = C0 + c, r0 = R0 + 32 * gc;
-        if (col < cols && r0 < rows) {         // rows % 32 == 0: the group is whole
-          float y[32];
+  // The 16 values this lane holds of group (block row br, block col bc) of
+  // the tile, in the D layout above: rotated when HAD, else read directly.
+  auto row_group = [&](int br, int bc, float* y) {     // row 32 br + n, columns 32 bc + ...
+    const uint16_t* base = tile + (32 * br + n) * kMxPitch + 32 * bc;
+    if constexpr (HAD) {
+      const u32x4_t b0 = *(const u32x4_t*)(base + 8 * half);
+      const u32x4_t b1 = *(const u32x4_t*)(base + 16 + 8 * half);
+      f32x16_t acc = {};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h0, __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(h1, __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
 #pragma unroll
-          for (int k = 0; k < 32; k++)
-            y[k] = __uint_as_float((uint32_t)tile[(32 * gc + k) * kMxPitch + c] << 16);
-          mx_rotate<HAD>(y);
-          uint32_t w[4];
-          const uint32_t code = mx_quant32(y, w);
-          *(uint4*)(codes_c + col * (rows / 2) + r0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
-          scales_c[col * (rows / 32) + r0 / 32] = (uint8_t)code;
-        }
-        __syncthreads();                       // LDS free for the next tile
+      for (int i = 0; i < 16; i++) y[i] = acc[i] * kInvSqrt32;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const u32x2_t w = *(const u32x2_t*)(base + 8 * q + 4 * half);
+        y[4 * q + 0] = bf16_lo(w.x);
+        y[4 * q + 1] = bf16_hi(w.x);
+        y[4 * q + 2] = bf16_lo(w.y);
+        y[4 * q + 3] = bf16_hi(w.y);
       }
     }
-    cur = nxt;
-    tcur = tnxt;
-    slot = next;
+  };
+  auto col_group = [&](int br, int bc, float* y) {     // column 32 bc + n, rows 32 br + ...
+    const uint16_t* base = tile + 32 * br * kMxPitch + 32 * bc + n;
+    if constexpr (HAD) {
+      uint32_t w[8];
+#pragma unroll
+      for (int p = 0; p < 8; p++) {          // B[k][n], k = 16 (p/4) + 8 half + 2 (p%4) + {0, 1}
+        const uint16_t* s = base + (16 * (p >> 2) + 8 * half + 2 * (p & 3)) * kMxPitch;
+        w[p] = (uint32_t)s[0] | ((uint32_t)s[kMxPitch] << 16);
+      }
+      f32x16_t acc = {};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          h0, __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3])), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          h1, __builtin_bit_cast(bf16x8_t, make_uint4(w[4], w[5], w[6], w[7])), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; i++) y[i] = acc[i] * kInvSqrt32;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        y[i] = __uint_as_float(
+            (uint32_t)base[(8 * (i >> 2) + 4 * half + (i & 3)) * kMxPitch] << 16);
+    }
+  };
+
+  // store offsets within a tile (per-thread constants): element e = t / 4
+  // (tile row or column), group g = t % 4
+  const int e = t >> 2, g = t & 3;
+  const int64_t sr_off = (int64_t)e * (cols / 2) + 16 * g, ss_off = (int64_t)e * (cols / 32) + g;
+  const int64_t sc_off = (int64_t)e * (rows / 2) + 16 * g, scs_off = (int64_t)e * (rows / 32) + g;
+
+  // Tile work; `to.ty < 0` (a slot with no tile) is uniform over the workgroup.
+  auto process = [&](Tile4& cur, const TileOrder& to) {
+    if (to.ty < 0) return;
+    const int64_t R0 = to.ty * kMxTile, C0 = to.tx * kMxTile;
+    static_for<4>([&](auto pc) {
+      constexpr int P = decltype(pc)::value;
+      const int p = t + kMxThreads * P;
+      *(u32x4_t*)(tile + (p >> 4) * kMxPitch + 8 * (p & 15)) = cur.template at<P>();
+    });
+    __syncthreads();
+    // wave w: row-wise blocks (w/2, 2 (w%2) + s), column-wise blocks (2 (w%2) + s, w/2)
+    const int bw = wave >> 1, bs = 2 * (wave & 1);
+    if constexpr (ROW) {
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        float y[16];
+        row_group(bw, bs + s, y);
+        uint32_t lo, hi, code;
+        mx_quant_pair(y, lo, hi, code);
+        const int r = 32 * bw + n;
+        *(u32x2_t*)(rcode + r * kMxCodePitch + 16 * (bs + s) + 8 * half) = u32x2_t{lo, hi};
+        if (is_a) rscale[4 * r + bs + s] = (uint8_t)code;
+      }
+    }
+    if constexpr (COL) {
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        float y[16];
+        col_group(bs + s, bw, y);
+        uint32_t lo, hi, code;
+        mx_quant_pair(y, lo, hi, code);
+        const int c = 32 * bw + n;
+        *(u32x2_t*)(ccode + c * kMxCodePitch + 16 * (bs + s) + 8 * half) = u32x2_t{lo, hi};
+        if (is_a) cscale[4 * c + bs + s] = (uint8_t)code;
+      }
+    }
+    __syncthreads();
+    // stores: thread t takes 16-byte segment t % 4 of tile row (column) t / 4,
+    // i.e. group t % 4; groups outside the tensor are skipped (cols % 32 == 0
+    // for row-wise and rows % 32 == 0 for column-wise output)
+    const int rem_r = (int)(rows - R0 < kMxTile ? rows - R0 : kMxTile);
+    const int rem_c = (int)(cols - C0 < kMxTile ? cols - C0 : kMxTile);
+    if constexpr (ROW) {
+      if (e < rem_r && 32 * g < rem_c) {
+        *(u32x4_t*)(codes_r + R0 * (cols / 2) + C0 / 2 + sr_off) =
+            *(const u32x4_t*)(rcode + e * kMxCodePitch + 16 * g);
+        scales_r[R0 * (cols / 32) + C0 / 32 + ss_off] = rscale[t];
+      }
+    }
+    if constexpr (COL) {
+      if (e < rem_c && 32 * g < rem_r) {
+        *(u32x4_t*)(codes_c + C0 * (rows / 2) + R0 / 2 + sc_off) =
+            *(const u32x4_t*)(ccode + e * kMxCodePitch + 16 * g);
+        scales_c[C0 * (rows / 32) + R0 / 32 + scs_off] = cscale[t];
+      }
+    }
+  };
+
+  // Two register sets in turn (no copy between them, so the wait for a
+  // tile's loads never includes the previous tile's stores).
+  Tile4 ta, tb;
+  TileOrder oa, ob;
+  uint32_t slot = blockIdx.x;
+  load(slot, ta, oa);
+  while (slot < nslots) {
+    const uint32_t s1 = slot + gridDim.x;      // grid is a multiple of 8: same XCD
+    load(s1, tb, ob);                          // in flight during this tile
+    process(ta, oa);
+    if (s1 >= nslots) break;
+    const uint32_t s2 = s1 + gridDim.x;
+    load(s2, ta, oa);
+    process(tb, ob);
+    slot = s2;
   }
 }
 
 inline void launch_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, bool had,
                          uint8_t* codes_r, uint8_t* scales_r, uint8_t* codes_c,
                          uint8_t* scales_c, hipStream_t st, int num_cus) {
-  const int64_t nslots = xcd_grid((rows + kMxRows - 1) / kMxRows, (cols + kMxTile - 1) / kMxTile,
-                                  kMxSuper * (kMxTile / kMxRows), kMxSuper);
+  const int64_t nslots = xcd_grid((rows + kMxTile - 1) / kMxTile, (cols + kMxTile - 1) / kMxTile,
+                                  kMxSuper, kMxSuper);
   // persistent: a multiple of 8 workgroups (XCD count)
   int64_t grid = (int64_t)num_cus * kMxWgPerCu;
   if (grid > nslots) grid = nslots;

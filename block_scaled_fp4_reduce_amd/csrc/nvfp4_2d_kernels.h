@@ -125,82 +125,90 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
     }
   };
 
-  Strips cur, nxt;
-  TileOrder tcur, tnxt;
-  uint32_t slot = blockIdx.x;
-  load(slot, cur, tcur);
-  while (slot < nslots) {
-    const uint32_t next = slot + gridDim.x;  // grid is a multiple of 8: same XCD
-    load(next, nxt, tnxt);
-    if (tcur.ty >= 0) {                      // uniform over the workgroup
-      const int64_t br = tcur.ty * 4 + wave;                 // tile row of this wave
-      const bool row_ok = br < brows;
-      const int64_t row = br * 16 + r;
+  // Tile work; `to.ty < 0` (a slot with no tile) is uniform over the workgroup.
+  auto process = [&](const Strips& cur, const TileOrder& to) {
+    if (to.ty < 0) return;
+    const int64_t br = to.ty * 4 + wave;                 // tile row of this wave
+    const bool row_ok = br < brows;
+    const int64_t row = br * 16 + r;
 #pragma unroll
-      for (int s = 0; s < k2dStrips; s++) {
-        const int64_t bc = (tcur.tx * k2dStrips + s) * 4 + tile;   // tile column
-        const bool ok = row_ok && bc < bcols;
-        const uint4 v0 = cur.v[2 * s], v1 = cur.v[2 * s + 1];
-        float y[16];
-        unpack8(v0, y);
-        unpack8(v1, y + 8);
-        float amax_r = 0.0f;
+    for (int s = 0; s < k2dStrips; s++) {
+      const int64_t bc = (to.tx * k2dStrips + s) * 4 + tile;   // tile column
+      const bool ok = row_ok && bc < bcols;
+      const uint4 v0 = cur.v[2 * s], v1 = cur.v[2 * s + 1];
+      float y[16];
+      unpack8(v0, y);
+      unpack8(v1, y + 8);
+      float amax_r = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; k++) amax_r = fmaxf(amax_r, fabsf(y[k]));
-        const float amax_b = tile_max(amax_r);
+      for (int k = 0; k < 16; k++) amax_r = fmaxf(amax_r, fabsf(y[k]));
+      const float amax_b = tile_max(amax_r);
 
-        uint32_t e6, e4;
-        e4m3_pair(amax_b * ts.k6, amax_b * ts.k4, e6, e4);
-        float2 sr = tab[e6];
-        uint32_t w0, w1, scale = e6, pick4 = 0;
-        const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
-        if constexpr (FOUR_SIX) {
-          const float2 sr4 = tab[e4];
-          uint32_t u0, u1;
-          const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
-          if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
-            w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
-          }
-        }
-        if (ok) {
-          *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
-          if (r == 0) {
-            scales[br * bcols + bc] = (uint8_t)scale;
-            if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
-          }
-        }
-        if constexpr (TRANSPOSE) {
-          // stage the tile (bf16, row r at st[16 r]), then lane r takes column r;
-          // each wave uses its own LDS slots, so a wave-level sync suffices
-          *(uint4*)(st + 16 * r) = v0;
-          *(uint4*)(st + 16 * r + 8) = v1;
-          wave_lds_sync();
-          float yc[16];
-#pragma unroll
-          for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
-          const float rr = sr.y;
-          uint32_t t0 = 0, t1 = 0;
-          t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
-          t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
-          t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
-          t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
-          t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
-          t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
-          t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
-          t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
-          if (ok) {
-            // column 16*tile + r, tile row br: 8 bytes; the 4 waves and the
-            // workgroup below (same XCD) complete the column's 64-byte segment
-            *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
-            if (r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
-          }
-          wave_lds_sync();                   // reads done before the next strip's writes
+      uint32_t e6, e4;
+      e4m3_pair(amax_b * ts.k6, amax_b * ts.k4, e6, e4);
+      float2 sr = tab[e6];
+      uint32_t w0, w1, scale = e6, pick4 = 0;
+      const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
+      if constexpr (FOUR_SIX) {
+        const float2 sr4 = tab[e4];
+        uint32_t u0, u1;
+        const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
+        if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
+          w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
         }
       }
+      if (ok) {
+        *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
+        if (r == 0) {
+          scales[br * bcols + bc] = (uint8_t)scale;
+          if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
+        }
+      }
+      if constexpr (TRANSPOSE) {
+        // stage the tile (bf16, row r at st[16 r]), then lane r takes column r;
+        // each wave uses its own LDS slots, so a wave-level sync suffices
+        *(uint4*)(st + 16 * r) = v0;
+        *(uint4*)(st + 16 * r + 8) = v1;
+        wave_lds_sync();
+        float yc[16];
+#pragma unroll
+        for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
+        const float rr = sr.y;
+        uint32_t t0 = 0, t1 = 0;
+        t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
+        t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
+        t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
+        t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
+        t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
+        t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
+        t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
+        t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
+        if (ok) {
+          // column 16*tile + r, tile row br: 8 bytes; the 4 waves and the
+          // workgroup below (same XCD) complete the column's 64-byte segment
+          *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
+          if (r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
+        }
+        wave_lds_sync();                   // reads done before the next strip's writes
+      }
     }
-    cur = nxt;
-    tcur = tnxt;
-    slot = next;
+  };
+
+  // Two register sets in turn (no copy between them, so the wait for a
+  // tile's loads never includes the previous tile's stores).
+  Strips sa, sb;
+  TileOrder oa, ob;
+  uint32_t slot = blockIdx.x;
+  load(slot, sa, oa);
+  while (slot < nslots) {
+    const uint32_t s1 = slot + gridDim.x;    // grid is a multiple of 8: same XCD
+    load(s1, sb, ob);
+    process(sa, oa);
+    if (s1 >= nslots) break;
+    const uint32_t s2 = s1 + gridDim.x;
+    load(s2, sa, oa);
+    process(sb, ob);
+    slot = s2;
   }
 }
 

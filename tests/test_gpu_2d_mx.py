@@ -1,12 +1,17 @@
 """GPU parity of the 16x16-tile NVFP4 path and of MXFP4 (row- and
 column-wise, with and without the 32-point Hadamard) against the CPU oracle.
-Both sides run the same fp32 operations, so every code and scale must match
-bit for bit."""
+Without rotation both sides run the same fp32 operations, so every code and
+scale must match bit for bit.  With the 32-point Hadamard the GPU sums on
+the matrix cores in another fp32 order than the oracle's butterfly, so codes
+and scales may differ only next to a rounding boundary or a power of two
+(see rotated_tolerance.py), at most 1e-5 of the elements, with the same
+dequantized error."""
 import numpy as np
 import pytest
 
 import oracle as O
 import synthetic as S
+from rotated_tolerance import check_mx_outputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -78,7 +83,8 @@ def test_2d_c3_full():
 
 # ------------------------------------------------------------ MXFP4
 MX_FLAGS = [fp4.ROWWISE, fp4.COLWISE, fp4.ROWWISE | fp4.COLWISE,
-            fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE, fp4.HAD32 | fp4.COLWISE]
+            fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE, fp4.HAD32 | fp4.COLWISE,
+            fp4.HAD32 | fp4.ROWWISE]
 
 
 @pytest.mark.parametrize("flags", MX_FLAGS)
@@ -89,8 +95,26 @@ def test_mx_parity(shape, flags):
     got = fp4.mxfp4_quantize(dev(x), flags)
     torch.cuda.synchronize()
     want = O.mxfp4_quantize(x, flags)
-    for k in want:
-        same(got[k], want[k], k)
+    mx_compare(x, flags, got, want, "mx %s" % (shape,))
+
+
+def mx_compare(x, flags, got, want, what):
+    if flags & fp4.HAD32:
+        print(what, check_mx_outputs(x, flags, got, want, host, what), flush=True)
+    else:
+        for k in want:
+            same(got[k], want[k], k)
+
+
+@pytest.mark.parametrize("flags", [fp4.ROWWISE, fp4.HAD32 | fp4.ROWWISE])
+@pytest.mark.parametrize("shape", [(1, 32), (45, 96), (200, 4128)])
+def test_mx_rowwise_ragged_rows(shape, flags):
+    """Row-wise output alone needs no row multiple: partial row blocks."""
+    x = S.gen("c5", *shape)
+    got = fp4.mxfp4_quantize(dev(x), flags)
+    torch.cuda.synchronize()
+    want = O.mxfp4_quantize(x, flags)
+    mx_compare(x, flags, got, want, "ragged %s" % (shape,))
 
 
 def test_mx_special_values_subnormal_groups():
@@ -100,8 +124,7 @@ def test_mx_special_values_subnormal_groups():
     for flags in (fp4.ROWWISE | fp4.COLWISE, fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE):
         got = fp4.mxfp4_quantize(dev(x), flags)
         want = O.mxfp4_quantize(x, flags)
-        for k in want:
-            same(got[k], want[k], k)
+        mx_compare(x, flags, got, want, "special")
 
 
 def test_mx_dequant_both_orientations():
@@ -111,8 +134,10 @@ def test_mx_dequant_both_orientations():
     want = O.mxfp4_quantize(x, f)
     dr = fp4.fp4_dequantize(fp4.FORMAT_MXFP4, got["codes_r"], got["scales_r"], None, 64, 96)
     dc = fp4.fp4_dequantize(fp4.FORMAT_MXFP4, got["codes_c"], got["scales_c"], None, 96, 64)
-    same(dr, O.dequantize(1, want["codes_r"], want["scales_r"], 0.0, 64, 96), "dequant rows")
-    same(dc, O.dequantize(1, want["codes_c"], want["scales_c"], 0.0, 96, 64), "dequant cols")
+    # the decode is exact: compare it with the oracle's decode of the GPU's own codes
+    same(dr, O.dequantize(1, host(got["codes_r"]), host(got["scales_r"]), 0.0, 64, 96), "dequant rows")
+    same(dc, O.dequantize(1, host(got["codes_c"]), host(got["scales_c"]), 0.0, 96, 64), "dequant cols")
+    mx_compare(x, f, got, want, "dequant case")
 
 
 def test_mx_c5_full():
@@ -121,5 +146,4 @@ def test_mx_c5_full():
     got = fp4.mxfp4_quantize(dev(x), f)
     torch.cuda.synchronize()
     want = O.mxfp4_quantize(x, f)
-    for k in want:
-        same(got[k], want[k], k)
+    mx_compare(x, f, got, want, "c5 full")
