@@ -33,6 +33,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# the kernel that does each workload's quantization (amax given)
+KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
+             "c2": "nvfp4_1d_kernel<true, false, false>",
+             "c3": "nvfp4_2d_kernel<true, true>",
+             "c4": "nvfp4_1d_kernel<false, true, true>",
+             "c5": "mxfp4_kernel<true, true, true>"}
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_4o6_8192x4096_counters.json")
 
@@ -175,25 +181,29 @@ def time_loop(torch, stream, fn, steps, warmup):
 
 
 def time_launches(torch, stream, fn, steps, warmup):
-    """Mean duration of single launches: an event pair on the launch stream
-    around every call, so inter-launch gaps are not counted."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        fn(i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps
+    """Mean time per launch of a single-kernel call: HIP events on the launch
+    stream around `steps` back-to-back launches (so it includes the short
+    dispatch gap between consecutive kernels; rocprofv3's kernel duration
+    excludes it)."""
+    ms, _ = time_loop(torch, stream, fn, steps, warmup)
+    return ms
+
+
+CAL_BYTES = 2 * 8192 * 4096          # one 64 MiB int16 tensor
+CAL_KERNEL = "BitwiseOr"               # name fragment of the calibration kernel
 
 
 def copy_reference(torch, row):
-    """Plain device copy of one input: the achievable bandwidth on this machine."""
+    """Plain device copy of one input: the achievable bandwidth on this machine.
+    Also runs, a few times, a 64 MiB elementwise bitwise-or (reads exactly
+    CAL_BYTES, writes exactly CAL_BYTES) whose kernel name is unique in a
+    profile: rocprofv3 FETCH_SIZE / WRITE_SIZE of the quantizers are scaled
+    by what the counters read for it."""
     src, dst = row.xs[1], row.xs[2].clone()
     ms, _ = time_loop(torch, row.stream, lambda i: dst.copy_(src), 20, 3)
+    for _ in range(3):
+        torch.bitwise_or(src, 0, out=dst)
+    torch.cuda.synchronize()
     return 2 * src.numel() * 2 / (ms * 1e-3) / 1e9
 
 
@@ -264,25 +274,30 @@ def summarize(out_path, dirs, command):
         lines += ["| kernel | grid | counter | KiB per dispatch (mean) |", "|---|---|---|---|"]
         for (k, cn, g), v in sorted(counters.items()):
             lines.append("| %s | %d | %s | %.1f |" % (k, g, cn, sum(v) / len(v)))
-        copy_bytes = 2 * 8192 * 4096                    # the benchmark's plain copy
         cal = {}
         for cn in ("FETCH_SIZE", "WRITE_SIZE"):
-            vs = [sum(v) / len(v) for (k, c2, g), v in counters.items()
-                  if c2 == cn and "copyBuffer" in k]
+            vs = [x for (k, c2, g), v in counters.items() if c2 == cn and CAL_KERNEL in k for x in v]
             if vs:
-                cal[cn] = copy_bytes / (max(vs) * 1024.0)
-        q = {cn: sum(v) / len(v) for (k, cn, g), v in counters.items()
-             if k.startswith("nvfp4_1d_kernel<true, false, false>")}
-        if cal and q:
-            fetch = q.get("FETCH_SIZE", 0) * 1024 * cal.get("FETCH_SIZE", 1)
-            write = q.get("WRITE_SIZE", 0) * 1024 * cal.get("WRITE_SIZE", 1)
-            lines += ["", "Calibration (plain 64 MiB copy): FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (
-                cal.get("FETCH_SIZE", 0), cal.get("WRITE_SIZE", 0)),
-                "4/6 quantize kernel per launch: fetched %.0f B, written %.0f B, total %.0f B "
-                "(algorithmic %d B)" % (fetch, write, fetch + write, algorithmic_bytes("c2"))]
-            result = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes": round(fetch),
-                      "write_bytes": round(write), "hbm_bytes_per_launch": round(fetch + write),
-                      "algorithmic_bytes": algorithmic_bytes("c2"), "command": command}
+                cal[cn] = CAL_BYTES / (sum(vs) / len(vs) * 1024.0)
+        if cal:
+            lines += ["", "Calibration (64 MiB int16 bitwise-or: %d B read, %d B written): "
+                      "FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (
+                          CAL_BYTES, CAL_BYTES, cal.get("FETCH_SIZE", 0), cal.get("WRITE_SIZE", 0)),
+                      "", "| workload | kernel | fetched B | written B | total B | algorithmic B | ratio |",
+                      "|---|---|---|---|---|---|---|"]
+            for wl, kern in KERNEL_OF.items():
+                q = {cn: sum(v) / len(v) for (k, cn, g), v in counters.items() if k.startswith(kern)}
+                if not q:
+                    continue
+                fetch = q.get("FETCH_SIZE", 0) * 1024 * cal.get("FETCH_SIZE", 1)
+                write = q.get("WRITE_SIZE", 0) * 1024 * cal.get("WRITE_SIZE", 1)
+                alg = algorithmic_bytes(wl)
+                lines.append("| %s | %s | %.0f | %.0f | %.0f | %d | %.3f |" % (
+                    ROWS[wl][4], kern, fetch, write, fetch + write, alg, (fetch + write) / alg))
+                if wl == "c2":
+                    result = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes": round(fetch),
+                              "write_bytes": round(write), "hbm_bytes_per_launch": round(fetch + write),
+                              "algorithmic_bytes": alg, "command": command}
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     if result:
@@ -344,7 +359,7 @@ def main():
                    "global_batch": 1, "parallelism": "none"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "quantize_kernel": {"us_avg": round(ms_kernel * 1e3, 3), "gbs": round(kernel_gbs, 2),
-                            "note": "amax given: one kernel per call, event pair per launch"},
+                            "note": "amax given: one kernel per call, mean over back-to-back launches"},
         "copy_kernel_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),

@@ -6,17 +6,18 @@
 // (a fixed, deterministic Hadamard rotation before quantizing, for both
 // operands of the weight-gradient product, hence both orientations).
 //
-// Mapping onto the chip.  A workgroup of 8 waves owns one 128x128 tile at a
-// time, staged through LDS in three steps, so every global access is a
-// full, coalesced segment (the kernel is bound by the memory pipeline, not
-// by arithmetic, once the rotation runs on the matrix cores):
-//  1. the tile is read with 16-byte non-temporal loads, 16 lanes per
+// Mapping onto the chip.  A workgroup of 8 waves owns a 256x256 region,
+// processed as four 128x128 tiles, each staged through LDS, so every global
+// access is a full, coalesced segment (the kernel is bound by the memory
+// pipeline, not by arithmetic, once the rotation runs on the matrix cores):
+//  1. a tile is read with 16-byte non-temporal loads, 16 lanes per
 //     256-byte row piece, and written to LDS (the next tile's loads are
 //     already in flight);
 //  2. each wave quantizes two 32x32 blocks row-wise and two column-wise,
-//     staging codes and scales in LDS;
-//  3. codes leave as 16-byte stores, four lanes per 64-byte row (or
-//     column) segment, and scales as bytes, four per row (or column).
+//     staging codes and scales of the whole region in LDS;
+//  3. after the region's fourth tile, every region row (and column) leaves
+//     as one full 128-byte code line (eight lanes of 16 bytes) and 8 scale
+//     bytes, so no output line is written in pieces from two places.
 // With the rotation, the 32-point transforms are dense 32x32 products (the
 // Hadamard matrix H, entries +-1, exact in bf16) on the matrix cores:
 // v_mfma_f32_32x32x16_bf16 twice per 32x32 block, products exact and sums
@@ -45,14 +46,21 @@ namespace fp4q {
 
 constexpr bool kHaveMx = true;
 #ifndef FP4Q_MX_WG_PER_CU
-#define FP4Q_MX_WG_PER_CU 2
+#define FP4Q_MX_WG_PER_CU 1
 #endif
-constexpr int kMxThreads = 512;                  // 8 waves
+#ifndef FP4Q_MX_WAVES
+#define FP4Q_MX_WAVES 8
+#endif
+constexpr int kMxWaves = FP4Q_MX_WAVES;          // 8 or 16 waves per workgroup
+constexpr int kMxThreads = 64 * kMxWaves;
+constexpr int kMxBlocksPerWave = 16 / kMxWaves;  // 32x32 blocks per wave and orientation
+constexpr int kMxPieces = 2048 / kMxThreads;     // 16-byte input pieces per thread and tile
 constexpr int kMxTile = 128;                     // tile rows and columns
+constexpr int kMxRegion = 256;                   // a workgroup's region: 2x2 tiles
 constexpr int kMxPitch = kMxTile + 8;            // bf16 per LDS row of the input tile
-constexpr int kMxCodePitch = 80;                 // bytes per LDS row of a code stage (64 + pad)
-constexpr int kMxSuper = 16;                     // 16x16 tiles per XCD super-tile
-constexpr int kMxWgPerCu = FP4Q_MX_WG_PER_CU;    // persistent workgroups per CU (LDS: 55 KiB each)
+constexpr int kMxCodePitch = 144;                // bytes per LDS row of a code stage (128 + pad)
+constexpr int kMxSuper = 8;                      // 8x8 regions per XCD super-tile
+constexpr int kMxWgPerCu = FP4Q_MX_WG_PER_CU;    // persistent workgroups per CU (LDS: 110 KiB each)
 
 // fp32 nearest to 1/sqrt(32) (bit pattern 0x3E3504F3): orthonormal H32.
 constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
@@ -120,8 +128,8 @@ __device__ __forceinline__ void mx_quant_pair(const float* y, uint32_t& lo, uint
   hi = (a >> 16) | (b & 0xFFFF0000u);
 }
 
-struct Tile4 {      // one thread's four 16-byte pieces of a tile (separate members:
-  u32x4_t v0, v1, v2, v3;   // never an indexed array)
+struct Tile4 {      // one thread's (up to) four 16-byte pieces of a tile (separate
+  u32x4_t v0, v1, v2, v3;   // members: never an indexed array)
   template <int P>
   __device__ __forceinline__ u32x4_t& at() {
     static_assert(P >= 0 && P < 4, "piece index");
@@ -138,44 +146,65 @@ __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
     uint8_t* __restrict__ scales_r, uint8_t* __restrict__ codes_c,
     uint8_t* __restrict__ scales_c) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kMxTile * kMxPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t rcode[ROW ? kMxTile * kMxCodePitch : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t ccode[COL ? kMxTile * kMxCodePitch : 16];
-  __shared__ uint8_t rscale[ROW ? kMxTile * 4 : 4];
-  __shared__ uint8_t cscale[COL ? kMxTile * 4 : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t rcode[ROW ? kMxRegion * kMxCodePitch : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ccode[COL ? kMxRegion * kMxCodePitch : 16];
+  __shared__ __attribute__((aligned(8))) uint8_t rscale[ROW ? kMxRegion * 8 : 8];
+  __shared__ __attribute__((aligned(8))) uint8_t cscale[COL ? kMxRegion * 8 : 8];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int n = lane & 31, half = lane >> 5;
   const bool is_a = half == 0;
-  const uint32_t TY = (uint32_t)((rows + kMxTile - 1) / kMxTile);
-  const uint32_t TX = (uint32_t)((cols + kMxTile - 1) / kMxTile);
-  const uint32_t nslots = (uint32_t)xcd_grid(TY, TX, kMxSuper, kMxSuper);
+  const uint32_t RY = (uint32_t)((rows + kMxRegion - 1) / kMxRegion);
+  const uint32_t RX = (uint32_t)((cols + kMxRegion - 1) / kMxRegion);
+  const uint32_t nslots = (uint32_t)xcd_grid(RY, RX, kMxSuper, kMxSuper);
+  const uint32_t G = gridDim.x;
   bf16x8_t h0 = {}, h1 = {};
   if constexpr (HAD) {
     h0 = had32_operand(lane, 0);
     h1 = had32_operand(lane, 1);
   }
 
-  // Piece p = t + 512 P of the tile: row p / 16 = t / 16 + 32 P, columns
-  // 8 (t % 16) .. +7.  Pieces outside the tensor read x[0..7] instead
+  // Work unit j of this workgroup: quadrant j % 4 of region slot
+  // blockIdx.x + (j / 4) G.  Quadrant q covers rows 128 (q / 2) and
+  // columns 128 (q % 2) of the region.
+  struct Unit {
+    int64_t R0, C0;      // tile origin (rows, columns); R0 < 0: no tile
+    int64_t RR0, CC0;    // region origin
+    int q;
+  };
+  auto unit = [&](uint32_t j) {
+    Unit u;
+    TileOrder to;
+    const uint32_t slot = blockIdx.x + (j >> 2) * G;
+    u.q = (int)(j & 3);
+    const bool valid = slot < nslots && xcd_tile<kMxSuper, kMxSuper>(slot, RY, RX, to);
+    u.RR0 = valid ? to.ty * kMxRegion : -1;
+    u.CC0 = valid ? to.tx * kMxRegion : -1;
+    u.R0 = u.RR0 + kMxTile * (u.q >> 1);
+    u.C0 = u.CC0 + kMxTile * (u.q & 1);
+    if (!valid || u.R0 >= rows || u.C0 >= cols) u.R0 = -1;
+    return u;
+  };
+
+  // Piece p = t + kMxThreads P of a tile: row p / 16 = t / 16 + (kMxThreads
+  // / 16) P, columns 8 (t % 16) .. +7.  Pieces outside the tensor read x[0..7] instead
   // (cols % 8 == 0 keeps a piece inside its row); their values are never
-  // stored.  Offsets within a tile are per-thread constants.
+  // stored.  Non-temporal: the input is read once, so it should not
+  // displace the output lines.
   const int lr = t >> 4, lc = 8 * (t & 15);
   const int64_t ld_off = (int64_t)lr * cols + lc;
-  auto load = [&](uint32_t slot, Tile4& v, TileOrder& to) {
-    const bool valid = slot < nslots && xcd_tile<kMxSuper, kMxSuper>(slot, TY, TX, to);
-    if (!valid) to.ty = to.tx = -1;
-    const int64_t R0 = valid ? to.ty * kMxTile : 0, C0 = valid ? to.tx * kMxTile : 0;
-    const uint16_t* base = x + R0 * cols + C0 + ld_off;
+  auto load = [&](const Unit& u, Tile4& v) {
+    const bool valid = u.R0 >= 0;
+    const uint16_t* base = x + (valid ? u.R0 * cols + u.C0 : 0) + ld_off;
     // rows / columns left from the tile origin, capped to 32 bits (uniform)
-    const int rem_r = valid ? (int)(rows - R0 < kMxTile ? rows - R0 : kMxTile) : 0;
-    const int rem_c = valid ? (int)(cols - C0 < kMxTile ? cols - C0 : kMxTile) : 0;
+    const int rem_r = valid ? (int)(rows - u.R0 < kMxTile ? rows - u.R0 : kMxTile) : 0;
+    const int rem_c = valid ? (int)(cols - u.C0 < kMxTile ? cols - u.C0 : kMxTile) : 0;
     const bool col_ok = lc < rem_c;
-    static_for<4>([&](auto pc) {
+    static_for<kMxPieces>([&](auto pc) {
       constexpr int P = decltype(pc)::value;
-      const bool ok = col_ok && lr + 32 * P < rem_r;
-      // non-temporal: the input is read once, so it should not displace the
-      // partially written code lines that L2 is combining
+      constexpr int dr = kMxThreads / 16 * P;
+      const bool ok = col_ok && lr + dr < rem_r;
       v.template at<P>() =
-          __builtin_nontemporal_load((const u32x4_t*)(ok ? base + (int64_t)32 * P * cols : x));
+          __builtin_nontemporal_load((const u32x4_t*)(ok ? base + (int64_t)dr * cols : x));
     });
   };
 
@@ -226,66 +255,79 @@ __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
     }
   };
 
-  // store offsets within a tile (per-thread constants): element e = t / 4
-  // (tile row or column), group g = t % 4
-  const int e = t >> 2, g = t & 3;
-  const int64_t sr_off = (int64_t)e * (cols / 2) + 16 * g, ss_off = (int64_t)e * (cols / 32) + g;
-  const int64_t sc_off = (int64_t)e * (rows / 2) + 16 * g, scs_off = (int64_t)e * (rows / 32) + g;
+  // store offsets within a region (per-thread constants): 16-byte code
+  // segment g = t % 8 of region row (column) t / 8 (+ kMxThreads / 8 per
+  // round), and scale byte t % 8 of the same row (column)
+  const int e0 = t >> 3, g = t & 7;
+  const int64_t sr_off = (int64_t)e0 * (cols / 2) + 16 * g, ss_off = (int64_t)e0 * (cols / 32) + g;
+  const int64_t sc_off = (int64_t)e0 * (rows / 2) + 16 * g, scs_off = (int64_t)e0 * (rows / 32) + g;
 
-  // Tile work; `to.ty < 0` (a slot with no tile) is uniform over the workgroup.
-  auto process = [&](Tile4& cur, const TileOrder& to) {
-    if (to.ty < 0) return;
-    const int64_t R0 = to.ty * kMxTile, C0 = to.tx * kMxTile;
-    static_for<4>([&](auto pc) {
-      constexpr int P = decltype(pc)::value;
-      const int p = t + kMxThreads * P;
-      *(u32x4_t*)(tile + (p >> 4) * kMxPitch + 8 * (p & 15)) = cur.template at<P>();
-    });
-    __syncthreads();
-    // wave w: row-wise blocks (w/2, 2 (w%2) + s), column-wise blocks (2 (w%2) + s, w/2)
-    const int bw = wave >> 1, bs = 2 * (wave & 1);
-    if constexpr (ROW) {
+  // Tile work: quantize into the region's LDS stage; after the fourth
+  // quadrant, write the region's outputs.  `u.R0 < 0` is uniform.
+  auto process = [&](Tile4& cur, const Unit& u) {
+    if (u.R0 >= 0) {
+      static_for<kMxPieces>([&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        const int p = t + kMxThreads * P;
+        *(u32x4_t*)(tile + (p >> 4) * kMxPitch + 8 * (p & 15)) = cur.template at<P>();
+      });
+      __syncthreads();
+      // wave w: row-wise blocks (bw, bs + s), column-wise blocks (bs + s, bw)
+      // with bw = w / (4 / B), bs = B (w % (4 / B)), B = kMxBlocksPerWave
+      constexpr int kPerRow = 4 / kMxBlocksPerWave;
+      const int bw = wave / kPerRow, bs = kMxBlocksPerWave * (wave % kPerRow);
+      const int qy = u.q >> 1, qx = u.q & 1;
+      if constexpr (ROW) {
 #pragma unroll
-      for (int s = 0; s < 2; s++) {
-        float y[16];
-        row_group(bw, bs + s, y);
-        uint32_t lo, hi, code;
-        mx_quant_pair(y, lo, hi, code);
-        const int r = 32 * bw + n;
-        *(u32x2_t*)(rcode + r * kMxCodePitch + 16 * (bs + s) + 8 * half) = u32x2_t{lo, hi};
-        if (is_a) rscale[4 * r + bs + s] = (uint8_t)code;
+        for (int s = 0; s < kMxBlocksPerWave; s++) {
+          float y[16];
+          row_group(bw, bs + s, y);
+          uint32_t lo, hi, code;
+          mx_quant_pair(y, lo, hi, code);
+          const int r = kMxTile * qy + 32 * bw + n;          // region row
+          *(u32x2_t*)(rcode + r * kMxCodePitch + 64 * qx + 16 * (bs + s) + 8 * half) =
+              u32x2_t{lo, hi};
+          if (is_a) rscale[8 * r + 4 * qx + bs + s] = (uint8_t)code;
+        }
       }
-    }
-    if constexpr (COL) {
+      if constexpr (COL) {
 #pragma unroll
-      for (int s = 0; s < 2; s++) {
-        float y[16];
-        col_group(bs + s, bw, y);
-        uint32_t lo, hi, code;
-        mx_quant_pair(y, lo, hi, code);
-        const int c = 32 * bw + n;
-        *(u32x2_t*)(ccode + c * kMxCodePitch + 16 * (bs + s) + 8 * half) = u32x2_t{lo, hi};
-        if (is_a) cscale[4 * c + bs + s] = (uint8_t)code;
+        for (int s = 0; s < kMxBlocksPerWave; s++) {
+          float y[16];
+          col_group(bs + s, bw, y);
+          uint32_t lo, hi, code;
+          mx_quant_pair(y, lo, hi, code);
+          const int c = kMxTile * qx + 32 * bw + n;          // region column
+          *(u32x2_t*)(ccode + c * kMxCodePitch + 64 * qy + 16 * (bs + s) + 8 * half) =
+              u32x2_t{lo, hi};
+          if (is_a) cscale[8 * c + 4 * qy + bs + s] = (uint8_t)code;
+        }
       }
+      __syncthreads();   // the next quadrant overwrites the tile
     }
-    __syncthreads();
-    // stores: thread t takes 16-byte segment t % 4 of tile row (column) t / 4,
-    // i.e. group t % 4; groups outside the tensor are skipped (cols % 32 == 0
-    // for row-wise and rows % 32 == 0 for column-wise output)
-    const int rem_r = (int)(rows - R0 < kMxTile ? rows - R0 : kMxTile);
-    const int rem_c = (int)(cols - C0 < kMxTile ? cols - C0 : kMxTile);
-    if constexpr (ROW) {
-      if (e < rem_r && 32 * g < rem_c) {
-        *(u32x4_t*)(codes_r + R0 * (cols / 2) + C0 / 2 + sr_off) =
-            *(const u32x4_t*)(rcode + e * kMxCodePitch + 16 * g);
-        scales_r[R0 * (cols / 32) + C0 / 32 + ss_off] = rscale[t];
+    if (u.q != 3 || u.RR0 < 0) return;
+    // region stores: every row (column) of the region leaves as one 128-byte
+    // code line and 8 scale bytes; outside the tensor nothing is stored
+    // (cols % 32 == 0 for row-wise and rows % 32 == 0 for column-wise output)
+    const int rem_r = (int)(rows - u.RR0 < kMxRegion ? rows - u.RR0 : kMxRegion);
+    const int rem_c = (int)(cols - u.CC0 < kMxRegion ? cols - u.CC0 : kMxRegion);
+    constexpr int kStep = kMxThreads / 8;                    // region rows per round
+#pragma unroll
+    for (int i = 0; i < kMxRegion / kStep; i++) {
+      const int e = e0 + kStep * i;
+      if constexpr (ROW) {
+        if (e < rem_r && 32 * g < rem_c) {
+          *(u32x4_t*)(codes_r + (u.RR0 + kStep * i) * (cols / 2) + u.CC0 / 2 + sr_off) =
+              *(const u32x4_t*)(rcode + e * kMxCodePitch + 16 * g);
+          scales_r[(u.RR0 + kStep * i) * (cols / 32) + u.CC0 / 32 + ss_off] = rscale[8 * e + g];
+        }
       }
-    }
-    if constexpr (COL) {
-      if (e < rem_c && 32 * g < rem_r) {
-        *(u32x4_t*)(codes_c + C0 * (rows / 2) + R0 / 2 + sc_off) =
-            *(const u32x4_t*)(ccode + e * kMxCodePitch + 16 * g);
-        scales_c[C0 * (rows / 32) + R0 / 32 + scs_off] = cscale[t];
+      if constexpr (COL) {
+        if (e < rem_c && 32 * g < rem_r) {
+          *(u32x4_t*)(codes_c + (u.CC0 + kStep * i) * (rows / 2) + u.RR0 / 2 + sc_off) =
+              *(const u32x4_t*)(ccode + e * kMxCodePitch + 16 * g);
+          scales_c[(u.CC0 + kStep * i) * (rows / 32) + u.RR0 / 32 + scs_off] = cscale[8 * e + g];
+        }
       }
     }
   };
@@ -293,26 +335,25 @@ __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
   // Two register sets in turn (no copy between them, so the wait for a
   // tile's loads never includes the previous tile's stores).
   Tile4 ta, tb;
-  TileOrder oa, ob;
-  uint32_t slot = blockIdx.x;
-  load(slot, ta, oa);
-  while (slot < nslots) {
-    const uint32_t s1 = slot + gridDim.x;      // grid is a multiple of 8: same XCD
-    load(s1, tb, ob);                          // in flight during this tile
-    process(ta, oa);
-    if (s1 >= nslots) break;
-    const uint32_t s2 = s1 + gridDim.x;
-    load(s2, ta, oa);
-    process(tb, ob);
-    slot = s2;
+  Unit ua = unit(0), ub;
+  load(ua, ta);
+  for (uint32_t j = 0;; j += 2) {
+    if (blockIdx.x + (j >> 2) * G >= nslots) break;
+    ub = unit(j + 1);
+    load(ub, tb);                              // in flight during this tile
+    process(ta, ua);
+    ua = unit(j + 2);
+    if (blockIdx.x + ((j + 1) >> 2) * G >= nslots) break;
+    load(ua, ta);
+    process(tb, ub);
   }
 }
 
 inline void launch_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, bool had,
                          uint8_t* codes_r, uint8_t* scales_r, uint8_t* codes_c,
                          uint8_t* scales_c, hipStream_t st, int num_cus) {
-  const int64_t nslots = xcd_grid((rows + kMxTile - 1) / kMxTile, (cols + kMxTile - 1) / kMxTile,
-                                  kMxSuper, kMxSuper);
+  const int64_t nslots = xcd_grid((rows + kMxRegion - 1) / kMxRegion,
+                                  (cols + kMxRegion - 1) / kMxRegion, kMxSuper, kMxSuper);
   // persistent: a multiple of 8 workgroups (XCD count)
   int64_t grid = (int64_t)num_cus * kMxWgPerCu;
   if (grid > nslots) grid = nslots;
