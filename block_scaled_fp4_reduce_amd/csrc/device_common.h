@@ -112,6 +112,22 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ---------------------------------------------------------------- register tiles
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // plain vectors: stay in VGPRs
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Tile4 {      // one thread's (up to) four 16-byte pieces of a tile (separate
+  u32x4_t v0, v1, v2, v3;   // members: never an indexed array)
+  template <int P>
+  __device__ __forceinline__ u32x4_t& at() {
+    static_assert(P >= 0 && P < 4, "piece index");
+    if constexpr (P == 0) return v0;
+    else if constexpr (P == 1) return v1;
+    else if constexpr (P == 2) return v2;
+    else return v3;
+  }
+};
+
 // ---------------------------------------------------------------- buffer access
 // Buffer resource over [base, base + bytes): loads past the end read 0 and
 // stores past the end are dropped, so tails need no branches.

@@ -67,8 +67,6 @@ constexpr float kInvSqrt32 = 0x1.6a09e6p-3f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // plain vector: stays in VGPRs
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // H[l % 32][16 h + 8 (l/32) + j] as bf16 +-1 (entries (-1)^popcount(m & k)).
 __device__ __forceinline__ bf16x8_t had32_operand(int lane, int h) {
@@ -127,18 +125,6 @@ __device__ __forceinline__ void mx_quant_pair(const float* y, uint32_t& lo, uint
   lo = (a & 0xFFFFu) | (b << 16);
   hi = (a >> 16) | (b & 0xFFFF0000u);
 }
-
-struct Tile4 {      // one thread's (up to) four 16-byte pieces of a tile (separate
-  u32x4_t v0, v1, v2, v3;   // members: never an indexed array)
-  template <int P>
-  __device__ __forceinline__ u32x4_t& at() {
-    static_assert(P >= 0 && P < 4, "piece index");
-    if constexpr (P == 0) return v0;
-    else if constexpr (P == 1) return v1;
-    else if constexpr (P == 2) return v2;
-    else return v3;
-  }
-};
 
 template <bool HAD, bool ROW, bool COL>
 __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
