@@ -197,16 +197,16 @@ __device__ __forceinline__ float sr_value(float t, uint64_t idx, uint32_t k0, ui
   const uint32_t w = philox_w0((uint32_t)idx, (uint32_t)(idx >> 32), 0u, 0u, k0, k1);
   const float u = (float)(w >> 8) * 0x1p-24f;
   const float a = fabsf(t);
-  float mag;
-  if (!(a < 6.0f)) {
-    mag = 6.0f;
-  } else {
-    const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
-    const float lo = a < 2.0f ? __builtin_floorf(a * 2.0f) * 0.5f
-                              : (a < 4.0f ? __builtin_floorf(a) : 4.0f);
-    const float p = (a - lo) / step;
-    mag = u < p ? lo + step : lo;
-  }
+  // grid spacing 0.5 / 1 / 2 on [0, 2) / [2, 4) / [4, 6): with inv = 1/spacing
+  // (2, 1 or 0.5), lo = floor(a * inv) / inv and p = (a - lo) * inv are exact
+  // (power-of-two scalings of exact values), i.e. the division of the
+  // definition done as a multiply
+  const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+  const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+  const float lo = __builtin_floorf(a * inv) * step;
+  const float p = (a - lo) * inv;
+  float mag = u < p ? lo + step : lo;
+  mag = a < 6.0f ? mag : 6.0f;                  // saturate (also NaN-free for Inf)
   return __builtin_copysignf(mag, t);
 }
 
