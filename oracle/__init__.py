@@ -76,6 +76,12 @@ def lib():
         L.orc_nvfp4_quantize.restype = C.c_int
         L.orc_nvfp4_quantize.argtypes = [u16p, C.c_int64, C.c_int64, C.c_uint32, C.c_uint64,
                                          f32p, f32p, u8p, u8p, u8p, u8p, u8p, C.c_void_p]
+        L.orc_nvfp4_quantize_f32.restype = C.c_int
+        L.orc_nvfp4_quantize_f32.argtypes = [f32p, C.c_int64, C.c_int64, C.c_uint32, C.c_uint64,
+                                             f32p, f32p, u8p, u8p, u8p]
+        L.orc_nvfp4_requantize_t.restype = C.c_int
+        L.orc_nvfp4_requantize_t.argtypes = [u8p, u8p, C.c_float, C.c_int64, C.c_int64,
+                                             C.c_uint32, C.c_uint64, f32p, u8p, u8p, u8p]
         L.orc_mxfp4_quantize.restype = C.c_int
         L.orc_mxfp4_quantize.argtypes = [u16p, C.c_int64, C.c_int64, C.c_uint32,
                                          u8p, u8p, u8p, u8p, f32p, f32p]
@@ -207,6 +213,42 @@ def nvfp4_quantize(x_bf16, flags=0, seed=0, amax=None, debug=False):
     for k, v in arrays.items():
         out["dbg_" + k] = v.reshape((rows, cols) if k in ("t", "u", "p") else scales.shape)
     return out
+
+
+def nvfp4_quantize_f32(x_f32, flags=0, seed=0, amax=None):
+    """NVFP4 of an fp32 tensor (1D flags); dict(codes, scales, alpha, choice)."""
+    x = np.ascontiguousarray(x_f32, dtype=np.float32)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    choice = np.zeros((rows, cols // 16), np.uint8)
+    alpha = np.zeros(1, np.float32)
+    amax_arr = None if amax is None else np.array([amax], np.float32)
+    rc = lib().orc_nvfp4_quantize_f32(
+        _p(x, C.c_float), rows, cols, flags, C.c_uint64(seed & (2**64 - 1)),
+        _p(amax_arr, C.c_float), _p(alpha, C.c_float), _p(codes, C.c_uint8),
+        _p(scales, C.c_uint8), _p(choice, C.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle nvfp4_quantize_f32 rejected the arguments (%d)" % rc)
+    return dict(codes=codes, scales=scales, alpha=np.float32(alpha[0]), choice=choice)
+
+
+def nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags=0, seed=0):
+    """NVFP4 (flags) of dequantize(X)^T for a 1D NVFP4 X [rows][cols]:
+    dict(codes [cols][rows/2], scales [cols][rows/16], alpha, choice)."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    ct = np.zeros((cols, rows // 2), np.uint8)
+    st = np.zeros((cols, rows // 16), np.uint8)
+    ch = np.zeros((cols, rows // 16), np.uint8)
+    a = np.zeros(1, np.float32)
+    rc = lib().orc_nvfp4_requantize_t(
+        _p(codes, C.c_uint8), _p(scales, C.c_uint8), C.c_float(alpha), rows, cols, flags,
+        C.c_uint64(seed & (2**64 - 1)), _p(a, C.c_float), _p(ct, C.c_uint8), _p(st, C.c_uint8),
+        _p(ch, C.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle nvfp4_requantize_t rejected the arguments (%d)" % rc)
+    return dict(codes=ct, scales=st, alpha=np.float32(a[0]), choice=ch)
 
 
 def mxfp4_quantize(x_bf16, flags=ROWWISE | COLWISE, debug=False):

@@ -206,13 +206,14 @@ static uint8_t get_nibble(const uint8_t* row, int64_t j) {
   return (j & 1) ? (uint8_t)(row[j >> 1] >> 4) : (uint8_t)(row[j >> 1] & 0x0Fu);
 }
 
-/* Convert the bf16 input to fp32 and apply the row rotation the flags ask
- * for (RHT16 on consecutive 16-value groups of each row). */
-static float* load_rotated(const uint16_t* x, int64_t rows, int64_t cols,
+/* Convert the input (bf16 x, or fp32 xf when x is NULL) to fp32 and apply
+ * the row rotation the flags ask for (RHT16 on consecutive 16-value groups
+ * of each row). */
+static float* load_rotated(const uint16_t* x, const float* xf, int64_t rows, int64_t cols,
                            uint32_t flags, uint64_t seed) {
   float* y = (float*)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
   if (!y) return NULL;
-  for (int64_t i = 0; i < rows * cols; i++) y[i] = bf16_to_f32(x[i]);
+  for (int64_t i = 0; i < rows * cols; i++) y[i] = x ? bf16_to_f32(x[i]) : xf[i];
   if (flags & ORC_RHT16) {
     const uint32_t signs = orc_rht16_signs(seed);
     float g[16];
@@ -243,7 +244,7 @@ static int nvfp4_flags_ok(int64_t rows, int64_t cols, uint32_t flags) {
 float orc_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols,
                       uint32_t flags, uint64_t seed) {
   if (!nvfp4_flags_ok(rows, cols, flags)) return NAN;
-  float* y = load_rotated(x, rows, cols, flags, seed);
+  float* y = load_rotated(x, NULL, rows, cols, flags, seed);
   float amax = 0.0f;
   for (int64_t i = 0; i < rows * cols; i++) {
     float a = fabsf(y[i]);
@@ -345,18 +346,19 @@ static block_result quantize_block(float* const* elems, int n, float amax_b,
   return br;
 }
 
-int orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
-                       uint32_t flags, uint64_t seed, const float* amax_in,
-                       float* alpha_out, uint8_t* codes, uint8_t* scales,
-                       uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
-                       orc_debug* dbg) {
+/* NVFP4 quantization of x (bf16) or, when x is NULL, of xf (fp32). */
+static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, int64_t cols,
+                              uint32_t flags, uint64_t seed, const float* amax_in,
+                              float* alpha_out, uint8_t* codes, uint8_t* scales,
+                              uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
+                              orc_debug* dbg) {
   if (!nvfp4_flags_ok(rows, cols, flags)) return -1;
   if (!codes || !scales || !alpha_out) return -2;
   const int two_d = (flags & ORC_BLOCK2D) != 0;
   const int four_six = (flags & ORC_FOUR_OVER_SIX) != 0;
   if (two_d && (flags & ORC_COLWISE) && (!codes_t || !scales_t)) return -2;
 
-  float* y = load_rotated(x, rows, cols, flags, seed);
+  float* y = load_rotated(x, xf, rows, cols, flags, seed);
   if (!y) return -3;
 
   /* Eq. 1: alpha = amax / (M_FP4 * M_FP8).  Reading: the scale maximum is
@@ -440,6 +442,55 @@ int orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
   }
   free(y);
   return 0;
+}
+
+int orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
+                       uint32_t flags, uint64_t seed, const float* amax_in,
+                       float* alpha_out, uint8_t* codes, uint8_t* scales,
+                       uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
+                       orc_debug* dbg) {
+  if (!x && rows * cols > 0) return -2;
+  return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, amax_in, alpha_out, codes,
+                            scales, choice, codes_t, scales_t, dbg);
+}
+
+int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t flags,
+                           uint64_t seed, const float* amax_in, float* alpha_out,
+                           uint8_t* codes, uint8_t* scales, uint8_t* choice) {
+  if (!x && rows * cols > 0) return -2;
+  if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
+  return nvfp4_quantize_any(NULL, x, rows, cols, flags, seed, amax_in, alpha_out, codes,
+                            scales, choice, NULL, NULL, NULL);
+}
+
+/* Requantization for the transposed operand of the backward pass ([QII]
+ * sec. 2: part of the data is quantized again; [NVFP4] sec. 7: the weight
+ * gradient contracts over the other dimension).  The input is a 1D NVFP4
+ * quantization of X [rows][cols]; the output is the NVFP4 quantization
+ * (flags: RTN6, FOUR_OVER_SIX, SR, RHT16) of the transpose of its
+ * dequantized values: quantize((dequantize(X))^T), blocks of 16 running
+ * along the original columns.  Output: codes_t [cols][rows/2], scales_t
+ * [cols][rows/16], choice_t likewise (may be NULL). */
+int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float alpha,
+                           int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                           float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
+                           uint8_t* choice_t) {
+  if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return -1;
+  if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
+  const size_t n = (size_t)(rows * cols > 0 ? rows * cols : 1);
+  float* xd = (float*)malloc(sizeof(float) * n);
+  float* xt = (float*)malloc(sizeof(float) * n);
+  if (!xd || !xt) { free(xd); free(xt); return -3; }
+  int rc = orc_dequantize(0, codes, scales, alpha, rows, cols, 0, xd);
+  if (rc == 0) {
+    for (int64_t r = 0; r < rows; r++)
+      for (int64_t c = 0; c < cols; c++) xt[c * rows + r] = xd[r * cols + c];
+    rc = nvfp4_quantize_any(NULL, xt, cols, rows, flags, seed, NULL, alpha_out, codes_t,
+                            scales_t, choice_t, NULL, NULL, NULL);
+  }
+  free(xd);
+  free(xt);
+  return rc;
 }
 
 /* ===================================================================== */

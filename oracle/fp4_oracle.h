@@ -17,6 +17,8 @@
  *          local encode scale applied per element).
  *  [MXFP4] AMD MI355X MXFP4 pretraining article (page 4), sec. 2
  *          (deterministic Hadamard rotation before MXFP4 quantization).
+ *  [QII]   Quartet II / MS-EDEN news article (page 1), sec. 2 (the backward
+ *          pass quantizes part of the data again).
  *  [Philox] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *          1, 2, 3", SC'11 (Philox4x32-10).
  *
@@ -99,6 +101,22 @@ int orc_mxfp4_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols,
 /* Dequantization. format 0 = NVFP4 (alpha used, BLOCK2D selects 16x16
  * tiles), 1 = MXFP4 (row-wise layout; pass the transposed shape for the
  * column-wise outputs). */
+/* NVFP4 quantization of an fp32 tensor (1D flags only: RTN6, FOUR_OVER_SIX,
+ * SR, RHT16); the same definition as orc_nvfp4_quantize on fp32 values. */
+int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t flags,
+                           uint64_t seed, const float* amax_in, float* alpha_out,
+                           uint8_t* codes, uint8_t* scales, uint8_t* choice);
+
+/* Requantize a 1D NVFP4 tensor X [rows][cols] (codes, scales, alpha) for the
+ * transposed operand: NVFP4 (flags as above) of dequantize(X)^T, giving
+ * codes_t [cols][rows/2], scales_t [cols][rows/16], choice_t (or NULL).
+ * rows % 16 == 0, cols % 16 == 0.  Parity pinned against the bf16 path on
+ * inputs whose dequantized values are bf16-exact (see the tests). */
+int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float alpha,
+                           int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                           float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
+                           uint8_t* choice_t);
+
 int orc_dequantize(int format, const uint8_t* codes, const uint8_t* scales,
                    float alpha, int64_t rows, int64_t cols, uint32_t flags,
                    float* out);
