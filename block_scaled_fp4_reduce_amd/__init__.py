@@ -32,8 +32,8 @@ FORMAT_MXFP4 = 1
 STATUS = {0: "FP4_OK", -1: "FP4_E_NULL", -2: "FP4_E_SHAPE", -3: "FP4_E_ALIGN",
           -4: "FP4_E_FLAGS", -5: "FP4_E_WORKSPACE", -6: "FP4_E_HIP"}
 
-EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "mxfp4_quantize",
-           "fp4_dequantize", "fp4_status_str", "fp4_abi_version")
+EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_requantize_t",
+           "mxfp4_quantize", "fp4_dequantize", "fp4_status_str", "fp4_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4q.so")
@@ -62,6 +62,8 @@ def lib():
         L.fp4_tensor_amax.argtypes = [vp, i64, i64, u32, u64, vp, vp, sz, vp]
         L.nvfp4_quantize.restype = C.c_int
         L.nvfp4_quantize.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.nvfp4_requantize_t.restype = C.c_int
+        L.nvfp4_requantize_t.argtypes = [vp, vp, vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, sz, vp]
         L.mxfp4_quantize.restype = C.c_int
         L.mxfp4_quantize.argtypes = [vp, i64, i64, u32, vp, vp, vp, vp, vp]
         L.fp4_dequantize.restype = C.c_int
@@ -166,6 +168,37 @@ def nvfp4_quantize(x, flags=0, seed=0, amax=None, want_choice=False, ws=None, st
         o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o.get("choice")),
         _ptr(o.get("codes_t")), _ptr(o.get("scales_t")), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return o
+
+
+def nvfp4_requantize_t(codes, scales, alpha, flags=0, seed=0, want_choice=False, ws=None,
+                       stream=None, out=None):
+    """NVFP4 of dequantize(X)^T for a 1D NVFP4 tensor X given as ``codes``
+    [rows][cols/2], ``scales`` [rows][cols/16] and ``alpha`` (1 float).
+    Returns a dict with ``codes`` [cols][rows/2], ``scales`` [cols][rows/16],
+    ``alpha`` and, when asked, ``choice``; ``out`` may supply these buffers."""
+    torch = _torch()
+    for t in (codes, scales, alpha):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous GPU tensors")
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or alpha.dtype != torch.float32:
+        raise TypeError("expected uint8 codes/scales and a float32 alpha")
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    if tuple(scales.shape) != (rows, cols // 16):
+        raise ValueError("scales must be [rows][cols/16]")
+    dev = codes.device
+    o = dict(out or {})
+    u8 = torch.uint8
+    o.setdefault("codes", torch.empty((cols, rows // 2), dtype=u8, device=dev))
+    o.setdefault("scales", torch.empty((cols, rows // 16), dtype=u8, device=dev))
+    o.setdefault("alpha", torch.empty(1, dtype=torch.float32, device=dev))
+    if want_choice:
+        o.setdefault("choice", torch.empty((cols, rows // 16), dtype=u8, device=dev))
+    ws = _workspace(rows, cols, flags, dev, ws)
+    _check("nvfp4_requantize_t", lib().nvfp4_requantize_t(
+        codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols, flags,
+        seed & (2**64 - 1), o["alpha"].data_ptr(), o["codes"].data_ptr(), o["scales"].data_ptr(),
+        _ptr(o.get("choice")), ws.data_ptr(), ws.numel(), _stream(stream)))
     return o
 
 

@@ -6,6 +6,7 @@
 #include "mx_kernels.h"
 #include "nvfp4_2d_kernels.h"
 #include "nvfp4_kernels.h"
+#include "requant_kernels.h"
 
 using namespace fp4q;
 
@@ -80,11 +81,31 @@ void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int na
       (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
+template <bool F46, bool SR, bool RHT>
+void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* alpha, int64_t rows,
+                    int64_t cols, uint32_t* ws, float* alpha_out, uint8_t* codes_t,
+                    uint8_t* scales_t, uint8_t* choice_t, uint64_t seed, hipStream_t st) {
+  const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
+  const int64_t tiles_x = cdiv(cols, kRqTileCols);
+  const int64_t ntiles = cdiv(rows, kRqTileRows) * tiles_x;
+  const int64_t resident = (int64_t)num_cus() * kRqWgPerCu;
+  int64_t ga = ntiles < kAmaxMaxGroups ? ntiles : kAmaxMaxGroups;
+  if (ga > resident) ga = resident;
+  if (ga < 1) ga = 1;
+  int64_t gq = ntiles < resident ? ntiles : resident;
+  if (gq < 1) gq = 1;
+  rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols,
+                                                          tiles_x, ntiles, ws, lo, hi);
+  rq_quant_kernel<F46, SR, RHT><<<(unsigned)gq, kRqThreads, 0, st>>>(
+      codes, scales, alpha, rows, cols, tiles_x, ntiles, ws, (int)ga, alpha_out, codes_t,
+      scales_t, choice_t, lo, hi);
+}
+
 }  // namespace
 
 extern "C" {
 
-int fp4_abi_version(void) { return 1; }
+int fp4_abi_version(void) { return 2; }
 
 const char* fp4_status_str(int status) {
   switch (status) {
@@ -170,6 +191,39 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
     launch_1d<false, false, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
   else
     launch_1d<false, false, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
+  return launched();
+}
+
+int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                       int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                       float* alpha_out, uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t,
+                       void* ws, size_t ws_bytes, void* stream) {
+  const int64_t n = rows * cols;
+  if (!alpha || !alpha_out || !ws) return FP4_E_NULL;
+  if (n > 0 && (!codes || !scales || !codes_t || !scales_t)) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  if (rows % 16 || cols % 16) return FP4_E_SHAPE;
+  if (flags & ~(uint32_t)(FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16)) return FP4_E_FLAGS;
+  if (int rc = check_nvfp4_flags(flags)) return rc;
+  if (!aligned(codes, 16) || !aligned(codes_t, 16) || !aligned(alpha, 4) ||
+      !aligned(alpha_out, 4) || !aligned(ws, 4))
+    return FP4_E_ALIGN;
+  if (ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t* w = (uint32_t*)ws;
+  const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
+  if (f46 && rht)
+    launch_requant<true, false, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+  else if (f46)
+    launch_requant<true, false, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+  else if (sr && rht)
+    launch_requant<false, true, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+  else if (sr)
+    launch_requant<false, true, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+  else if (rht)
+    launch_requant<false, false, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+  else
+    launch_requant<false, false, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
   return launched();
 }
 

@@ -117,6 +117,34 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                    uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Requantization of a 1D NVFP4 tensor for the transposed operand: the
+ * NVFP4 quantization of dequantize(X)^T, with its own tensor scale.  The
+ * backward pass quantizes data a second time (Quartet II / MS-EDEN
+ * article, sec. 2); the weight gradient contracts over the other
+ * dimension, so its operand needs blocks along the other axis (NVIDIA
+ * NVFP4 article, sec. 7).  Dequantization is q * (alpha * Delta) in fp32
+ * (NVIDIA NVFP4 article, sec. 6); the result equals nvfp4_quantize applied
+ * to that fp32 transpose ("Four Over Six" Eq. 1-3), bit for bit.
+ *   codes, scales, alpha  the input as a 1D nvfp4_quantize writes it:
+ *             codes [rows][cols/2], scales [rows][cols/16] (finite E4M3
+ *             codes; the sign bit is ignored, 0x7F is outside the domain),
+ *             alpha one device float.
+ *   flags     FP4_RTN6 or FOUR_OVER_SIX, SR, RHT16, as for a 1D
+ *             nvfp4_quantize (SR|FOUR_OVER_SIX rejected); BLOCK2D, COLWISE,
+ *             ROWWISE and HAD32 rejected.
+ *   seed      Philox key: SR counter = element index in the output
+ *             (out_row * rows + out_col); RHT16 signs as nvfp4_quantize.
+ *             The rotation runs along output rows.
+ *   alpha_out one device float: the output's tensor scale.
+ *   codes_t   [cols][rows/2];  scales_t [cols][rows/16];
+ *   choice_t  NULL or [cols][rows/16], 1 where the block took M = 4.
+ *   ws        fp4_workspace_bytes(rows, cols, flags) bytes (device).
+ *   Shapes: rows % 16 == 0 and cols % 16 == 0. */
+int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                       int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                       float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
+                       uint8_t* choice_t, void* ws, size_t ws_bytes, void* stream);
+
 /* MXFP4 quantization (NVIDIA NVFP4 article sec. 1 and 5; AMD MI355X MXFP4
  * article sec. 2).  Per 32 values: optional 32-point Hadamard (FP4_HAD32,
  * orthonormal), exponent e = floor(log2(amax)) - 2 (UE8M0 code e + 127,

@@ -122,3 +122,15 @@ def special_values_tensor(rows: int, cols: int, seed: int = 7) -> np.ndarray:
                 bits[r, sl] = f32_to_bf16_bits(w)
             # kinds 6, 7: plain normals
     return bits
+
+
+def random_nvfp4(rows: int, cols: int, seed: int = 3, zero_frac: float = 0.02):
+    """Bytes of an arbitrary 1D NVFP4 tensor [rows][cols]: uniform random
+    packed codes (every nibble, both signs) and E4M3 scale codes 1..126
+    (normal and subnormal, never the NaN code), with a fraction of blocks
+    given scale code 0.  Returns (codes [rows][cols/2], scales [rows][cols/16])."""
+    rng = _rng(seed)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(1, 127, size=(rows, cols // 16), dtype=np.uint8)
+    scales[rng.random(scales.shape) < zero_frac] = 0
+    return codes, scales

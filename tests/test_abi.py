@@ -37,7 +37,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.fp4_abi_version() == 1
+    assert L.fp4_abi_version() == 2
     for code in fp4.STATUS:
         assert L.fp4_status_str(code)
     assert L.fp4_status_str(E_SHAPE) != L.fp4_status_str(E_FLAGS)
@@ -84,6 +84,32 @@ def test_amax_rejects(L):
     assert L.fp4_tensor_amax(P, 32, 64, fp4.HAD32, 0, F4, P, 4096, None) == E_FLAGS
     assert L.fp4_tensor_amax(P + 4, 32, 64, 0, 0, F4, P, 4096, None) == E_ALIGN
     assert L.fp4_tensor_amax(P, 32, 64, 0, 0, F4, P, 8, None) == E_WS
+
+
+def rq(L, codes=P, scales=P, alpha=F4, rows=32, cols=64, flags=0, alpha_out=F4, ct=P, st=P,
+       choice=None, ws=P, wsb=1 << 20):
+    return L.nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags, 0, alpha_out, ct, st,
+                                choice, ws, wsb, None)
+
+
+def test_requant_rejects(L):
+    assert rq(L, codes=None) == E_NULL
+    assert rq(L, scales=None) == E_NULL
+    assert rq(L, alpha=None) == E_NULL
+    assert rq(L, alpha_out=None) == E_NULL
+    assert rq(L, ct=None) == E_NULL
+    assert rq(L, st=None) == E_NULL
+    assert rq(L, ws=None) == E_NULL
+    assert rq(L, rows=24) == E_SHAPE                        # rows % 16
+    assert rq(L, cols=40) == E_SHAPE                        # cols % 16
+    assert rq(L, rows=-16) == E_SHAPE
+    assert rq(L, rows=1 << 21, cols=1 << 20) == E_SHAPE     # 2^41 elements
+    for f in (fp4.BLOCK2D, fp4.COLWISE, fp4.ROWWISE, fp4.HAD32, fp4.SR | fp4.FOUR_OVER_SIX, 1 << 9):
+        assert rq(L, flags=f) == E_FLAGS, f
+    assert rq(L, codes=Q) == E_ALIGN
+    assert rq(L, ct=Q) == E_ALIGN
+    assert rq(L, alpha=F4 + 1) == E_ALIGN
+    assert rq(L, wsb=16) == E_WS
 
 
 def test_mx_rejects(L):

@@ -18,12 +18,7 @@ FLAGS = [0, O.FOUR_OVER_SIX, O.SR, O.RHT16, O.RHT16 | O.SR]
 
 
 def random_nvfp4(rows, cols, seed=3):
-    rng = np.random.default_rng(seed)
-    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
-    # E4M3 scale codes 1..126 (normal and subnormal, no NaN); a few zero blocks
-    scales = rng.integers(1, 127, size=(rows, cols // 16), dtype=np.uint8)
-    scales[rng.random(scales.shape) < 0.02] = 0
-    return codes, scales
+    return S.random_nvfp4(rows, cols, seed)
 
 
 @pytest.mark.parametrize("flags", FLAGS)
