@@ -15,7 +15,9 @@ read + FP4 codes + E4M3 scales + 4 B tensor scale), the fraction of the
 8 TB/s HBM peak, the quantize kernel alone (amax given) timed with HIP
 events on its stream, rocprofv3 traffic for that kernel (when the committed
 counter summary matches the current kernel sources), the same figures for
-the other four workloads under "rows", and the CPU oracle timed on the host.
+the other four workloads and for the requantization of a quantized
+activation and gradient for the transposed operand under "rows", and the CPU
+oracle timed on the host.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-rows]
     python bench.py --summarize OUT.md DIR [DIR...]   # rocprofv3 output -> summary
@@ -38,7 +40,9 @@ KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c2": "nvfp4_1d_kernel<true, false, false>",
              "c3": "nvfp4_2d_kernel<true, true>",
              "c4": "nvfp4_1d_kernel<false, true, true>",
-             "c5": "mxfp4_kernel<true, true, true>"}
+             "c5": "mxfp4_kernel<true, true, true>",
+             "f4a": "rq_quant_kernel<true, false, true>",
+             "f4g": "rq_quant_kernel<false, true, true>"}
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_4o6_8192x4096_counters.json")
 
@@ -49,13 +53,21 @@ ROWS = {
     "c3": (14336, 4096, "nvfp4", 1 | 8 | 64, "nvfp4_2d16x16_four_over_six_transposed_14336x4096"),
     "c4": (8192, 14336, "nvfp4", 2 | 4, "nvfp4_rht16_sr_8192x14336"),
     "c5": (16384, 8192, "mxfp4", 16 | 32 | 64, "mxfp4_had32_row_col_16384x8192"),
+    # requantization of a 1D NVFP4 tensor for the transposed operand; the
+    # input is the activation (4/6) or the gradient (RHT16 + SR) quantized
+    "f4a": (8192, 4096, "requant", 1 | 4, "nvfp4_requant_t_rht16_four_over_six_8192x4096"),
+    "f4g": (8192, 14336, "requant", 2 | 4, "nvfp4_requant_t_rht16_sr_8192x14336"),
 }
+# requant workload -> (workload whose quantization is the input, its flags)
+REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
 SEED = 0x0123456789ABCDEF
 
 
 def algorithmic_bytes(wl):
     rows, cols, kind, flags, _ = ROWS[wl]
     n = rows * cols
+    if kind == "requant":                            # NVFP4 in, NVFP4 of the transpose out
+        return 2 * (n // 2 + n // 16 + 4)
     if kind == "mxfp4":
         return 2 * n + 2 * (n // 2 + n // 32)
     if flags & 8:                                    # 16x16 tiles
@@ -96,17 +108,20 @@ class Row:
         rows, cols, kind, flags, label = ROWS[wl]
         self.rows, self.cols, self.kind, self.flags, self.label = rows, cols, kind, flags, label
         dev = torch.device("cuda:0")
+        L = fp4.lib()
+        self.L = L
+        self.stream = torch.cuda.current_stream()
+        self.sp = self.stream.cuda_stream
+        u8 = torch.uint8
+        if kind == "requant":
+            self._init_requant(fp4, torch, synthetic, np, dev)
+            return
         x_np = synthetic.gen(wl)
         self.x_np = x_np
         x0 = torch.from_numpy(x_np.view(np.int16)).to(dev)
         nbytes = x0.numel() * 2
         self.nbuf = min(64, max(4, -(-(1 << 30) // nbytes)))   # >= 1 GiB of inputs (c1: 64 copies)
         self.xs = [x0] + [x0.clone() for _ in range(self.nbuf - 1)]
-        L = fp4.lib()
-        self.L = L
-        self.stream = torch.cuda.current_stream()
-        self.sp = self.stream.cuda_stream
-        u8 = torch.uint8
         self.outs = []
         if kind == "nvfp4":
             two_d = bool(flags & 8)
@@ -154,6 +169,40 @@ class Row:
                 self.args_step.append(a)
                 self.args_kernel.append(a)
         self.fn = L.nvfp4_quantize if kind == "nvfp4" else L.mxfp4_quantize
+        torch.cuda.synchronize()
+
+    def _init_requant(self, fp4, torch, synthetic, np, dev):
+        """Inputs: the source workload quantized by the library, copied to
+        >= 1 GiB of resident buffers; outputs preallocated per copy."""
+        rows, cols, flags = self.rows, self.cols, self.flags
+        src, sflags = REQUANT_SRC[self.wl]
+        self.x_np = synthetic.gen(src)
+        q = fp4.nvfp4_quantize(torch.from_numpy(self.x_np.view(np.int16)).to(dev), sflags, seed=SEED)
+        per = rows * cols // 2 + rows * cols // 16
+        self.nbuf = min(64, max(4, -(-(1 << 30) // per)))
+        u8, f32 = torch.uint8, torch.float32
+        self.ins = [q] + [{k: v.clone() for k, v in q.items()} for _ in range(self.nbuf - 1)]
+        self.outs = [dict(codes=torch.empty((cols, rows // 2), dtype=u8, device=dev),
+                          scales=torch.empty((cols, rows // 16), dtype=u8, device=dev),
+                          alpha=torch.empty(1, dtype=f32, device=dev),
+                          amax=torch.empty(1, dtype=f32, device=dev)) for _ in range(self.nbuf)]
+        L = self.L
+        self.ws = torch.empty(max(16, L.fp4_workspace_bytes(rows, cols, flags)), dtype=u8, device=dev)
+        self.args_step, self.args_kernel = [], []
+        for k in range(self.nbuf):
+            i, o = self.ins[k], self.outs[k]
+            head = (i["codes"].data_ptr(), i["scales"].data_ptr(), i["alpha"].data_ptr(), rows, cols,
+                    flags, SEED)
+            tail = (o["alpha"].data_ptr(), o["codes"].data_ptr(), o["scales"].data_ptr(), None)
+            self.args_step.append(head + (None,) + tail + (self.ws.data_ptr(), self.ws.numel(), self.sp))
+            self.args_kernel.append(head + (o["amax"].data_ptr(),) + tail + (None, 0, self.sp))
+        self.fn = L.nvfp4_requantize_t
+        # the quantize pass alone runs with an amax given: the output's own
+        # (recovered from its tensor scale; the work does not depend on it)
+        C = 256.0 if flags & 1 else 448.0
+        for k in range(self.nbuf):
+            self.step(k)
+            torch.mul(self.outs[k]["alpha"], 6.0 * C, out=self.outs[k]["amax"])
         torch.cuda.synchronize()
 
     def step(self, i):
@@ -219,9 +268,14 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
     times = []
     t_end = time.time() + budget_s
     while len(times) < 5 and (time.time() < t_end or len(times) < 1):
+        if kind == "requant" and not times:                  # the input, made by the oracle
+            q = oracle.nvfp4_quantize(x, REQUANT_SRC[wl][1], seed=SEED)
         t0 = time.perf_counter()
         if kind == "nvfp4":
             oracle.nvfp4_quantize(x, flags, seed=SEED)
+        elif kind == "requant":
+            oracle.nvfp4_requantize_t(q["codes"], q["scales"], q["alpha"], x.shape[0], cols, flags,
+                                      seed=SEED)
         else:
             oracle.mxfp4_quantize(x, flags)
         times.append(time.perf_counter() - t0)
@@ -368,7 +422,7 @@ def main():
     }
     if not args.no_rows:
         rows = []
-        for wl in ("c1", "c3", "c4", "c5"):
+        for wl in ("c1", "c3", "c4", "c5", "f4a", "f4g"):
             r = Row(wl, fp4, torch, synthetic, np)
             st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
             kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)

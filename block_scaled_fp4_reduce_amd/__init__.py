@@ -63,7 +63,8 @@ def lib():
         L.nvfp4_quantize.restype = C.c_int
         L.nvfp4_quantize.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.nvfp4_requantize_t.restype = C.c_int
-        L.nvfp4_requantize_t.argtypes = [vp, vp, vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, sz, vp]
+        L.nvfp4_requantize_t.argtypes = [vp, vp, vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, sz,
+                                         vp]
         L.mxfp4_quantize.restype = C.c_int
         L.mxfp4_quantize.argtypes = [vp, i64, i64, u32, vp, vp, vp, vp, vp]
         L.fp4_dequantize.restype = C.c_int
@@ -171,12 +172,13 @@ def nvfp4_quantize(x, flags=0, seed=0, amax=None, want_choice=False, ws=None, st
     return o
 
 
-def nvfp4_requantize_t(codes, scales, alpha, flags=0, seed=0, want_choice=False, ws=None,
-                       stream=None, out=None):
+def nvfp4_requantize_t(codes, scales, alpha, flags=0, seed=0, amax=None, want_choice=False,
+                       ws=None, stream=None, out=None):
     """NVFP4 of dequantize(X)^T for a 1D NVFP4 tensor X given as ``codes``
     [rows][cols/2], ``scales`` [rows][cols/16] and ``alpha`` (1 float).
     Returns a dict with ``codes`` [cols][rows/2], ``scales`` [cols][rows/16],
-    ``alpha`` and, when asked, ``choice``; ``out`` may supply these buffers."""
+    ``alpha`` and, when asked, ``choice``; ``out`` may supply these buffers.
+    ``amax`` (1 float) skips the amax pass."""
     torch = _torch()
     for t in (codes, scales, alpha):
         if not t.is_cuda or not t.is_contiguous():
@@ -194,11 +196,13 @@ def nvfp4_requantize_t(codes, scales, alpha, flags=0, seed=0, want_choice=False,
     o.setdefault("alpha", torch.empty(1, dtype=torch.float32, device=dev))
     if want_choice:
         o.setdefault("choice", torch.empty((cols, rows // 16), dtype=u8, device=dev))
-    ws = _workspace(rows, cols, flags, dev, ws)
+    if amax is None:
+        ws = _workspace(rows, cols, flags, dev, ws)
     _check("nvfp4_requantize_t", lib().nvfp4_requantize_t(
         codes.data_ptr(), scales.data_ptr(), alpha.data_ptr(), rows, cols, flags,
-        seed & (2**64 - 1), o["alpha"].data_ptr(), o["codes"].data_ptr(), o["scales"].data_ptr(),
-        _ptr(o.get("choice")), ws.data_ptr(), ws.numel(), _stream(stream)))
+        seed & (2**64 - 1), _ptr(amax), o["alpha"].data_ptr(), o["codes"].data_ptr(),
+        o["scales"].data_ptr(), _ptr(o.get("choice")), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(stream)))
     return o
 
 

@@ -83,21 +83,28 @@ void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int na
 
 template <bool F46, bool SR, bool RHT>
 void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* alpha, int64_t rows,
-                    int64_t cols, uint32_t* ws, float* alpha_out, uint8_t* codes_t,
-                    uint8_t* scales_t, uint8_t* choice_t, uint64_t seed, hipStream_t st) {
+                    int64_t cols, const float* amax_in, uint32_t* ws, float* alpha_out,
+                    uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t, uint64_t seed,
+                    hipStream_t st) {
   const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
   const int64_t tiles_x = cdiv(cols, kRqTileCols);
   const int64_t ntiles = cdiv(rows, kRqTileRows) * tiles_x;
   const int64_t resident = (int64_t)num_cus() * kRqWgPerCu;
-  int64_t ga = ntiles < kAmaxMaxGroups ? ntiles : kAmaxMaxGroups;
-  if (ga > resident) ga = resident;
-  if (ga < 1) ga = 1;
+  const uint32_t* abits = (const uint32_t*)amax_in;
+  int namax = 1;
+  if (!amax_in) {
+    int64_t ga = ntiles < kRqAmaxGroups ? ntiles : kRqAmaxGroups;
+    if (ga > resident) ga = resident;
+    if (ga < 1) ga = 1;
+    rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols,
+                                                            tiles_x, ntiles, ws, lo, hi);
+    abits = ws;
+    namax = (int)ga;
+  }
   int64_t gq = ntiles < resident ? ntiles : resident;
   if (gq < 1) gq = 1;
-  rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols,
-                                                          tiles_x, ntiles, ws, lo, hi);
   rq_quant_kernel<F46, SR, RHT><<<(unsigned)gq, kRqThreads, 0, st>>>(
-      codes, scales, alpha, rows, cols, tiles_x, ntiles, ws, (int)ga, alpha_out, codes_t,
+      codes, scales, alpha, rows, cols, tiles_x, ntiles, abits, namax, alpha_out, codes_t,
       scales_t, choice_t, lo, hi);
 }
 
@@ -123,7 +130,8 @@ const char* fp4_status_str(int status) {
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
   (void)rows; (void)cols;
   if (flags & FP4_HAD32) return 0;
-  return (size_t)kAmaxMaxGroups * sizeof(uint32_t);
+  const int groups = kAmaxMaxGroups > kRqAmaxGroups ? kAmaxMaxGroups : kRqAmaxGroups;
+  return (size_t)groups * sizeof(uint32_t);
 }
 
 int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -196,34 +204,33 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
 
 int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,
                        int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
-                       float* alpha_out, uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t,
-                       void* ws, size_t ws_bytes, void* stream) {
+                       const float* amax_in, float* alpha_out, uint8_t* codes_t,
+                       uint8_t* scales_t, uint8_t* choice_t, void* ws, size_t ws_bytes,
+                       void* stream) {
   const int64_t n = rows * cols;
-  if (!alpha || !alpha_out || !ws) return FP4_E_NULL;
+  if (!alpha || !alpha_out || (!amax_in && !ws)) return FP4_E_NULL;
   if (n > 0 && (!codes || !scales || !codes_t || !scales_t)) return FP4_E_NULL;
   if (int rc = check_shape(rows, cols)) return rc;
   if (rows % 16 || cols % 16) return FP4_E_SHAPE;
   if (flags & ~(uint32_t)(FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16)) return FP4_E_FLAGS;
   if (int rc = check_nvfp4_flags(flags)) return rc;
   if (!aligned(codes, 16) || !aligned(codes_t, 16) || !aligned(alpha, 4) ||
-      !aligned(alpha_out, 4) || !aligned(ws, 4))
+      !aligned(alpha_out, 4) || !aligned(amax_in, 4) || !aligned(ws, 4))
     return FP4_E_ALIGN;
-  if (ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
+  if (!amax_in && ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   uint32_t* w = (uint32_t*)ws;
   const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
-  if (f46 && rht)
-    launch_requant<true, false, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
-  else if (f46)
-    launch_requant<true, false, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
-  else if (sr && rht)
-    launch_requant<false, true, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
-  else if (sr)
-    launch_requant<false, true, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
-  else if (rht)
-    launch_requant<false, false, true>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
-  else
-    launch_requant<false, false, false>(codes, scales, alpha, rows, cols, w, alpha_out, codes_t, scales_t, choice_t, seed, st);
+#define FP4Q_RQ(F, S, R)                                                                     \
+  launch_requant<F, S, R>(codes, scales, alpha, rows, cols, amax_in, w, alpha_out, codes_t, \
+                          scales_t, choice_t, seed, st)
+  if (f46 && rht) FP4Q_RQ(true, false, true);
+  else if (f46) FP4Q_RQ(true, false, false);
+  else if (sr && rht) FP4Q_RQ(false, true, true);
+  else if (sr) FP4Q_RQ(false, true, false);
+  else if (rht) FP4Q_RQ(false, false, true);
+  else FP4Q_RQ(false, false, false);
+#undef FP4Q_RQ
   return launched();
 }
 

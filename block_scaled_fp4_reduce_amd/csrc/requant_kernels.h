@@ -30,6 +30,7 @@ constexpr int kRqThreads = 512;
 constexpr int kRqTileRows = 256;   // 16 segments of 16 input rows
 constexpr int kRqTileCols = 256;   // 32 groups of 8 input columns
 constexpr int kRqWgPerCu = 2;
+constexpr int kRqAmaxGroups = 1024;   // most partial maxima the amax pass writes
 
 // The 16 dequantized values of column pair B of the thread's 8 columns
 // (columns 2B and 2B+1) down its 16 rows.

@@ -76,8 +76,9 @@ enum {
 
 enum { FP4_FORMAT_NVFP4 = 0, FP4_FORMAT_MXFP4 = 1 };
 
-/* Bytes of device workspace nvfp4_quantize (with amax_in == NULL) and
- * fp4_tensor_amax need for this shape and these flags; 0 if none.  The
+/* Bytes of device workspace nvfp4_quantize and nvfp4_requantize_t (with
+ * amax_in == NULL) and fp4_tensor_amax need for this shape and these
+ * flags; 0 if none.  The
  * workspace needs no initialisation and is scratch for the duration of the
  * call (stream order). */
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags);
@@ -135,15 +136,20 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
  *   seed      Philox key: SR counter = element index in the output
  *             (out_row * rows + out_col); RHT16 signs as nvfp4_quantize.
  *             The rotation runs along output rows.
+ *   amax_in   NULL: the output's largest magnitude (after RHT16 when
+ *             asked) is computed here (one extra read of the input, needs
+ *             `ws`); else one device float taken as that magnitude.
  *   alpha_out one device float: the output's tensor scale.
  *   codes_t   [cols][rows/2];  scales_t [cols][rows/16];
  *   choice_t  NULL or [cols][rows/16], 1 where the block took M = 4.
- *   ws        fp4_workspace_bytes(rows, cols, flags) bytes (device).
+ *   ws        fp4_workspace_bytes(rows, cols, flags) bytes (device), or
+ *             NULL with amax_in.
  *   Shapes: rows % 16 == 0 and cols % 16 == 0. */
 int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,
                        int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
-                       float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
-                       uint8_t* choice_t, void* ws, size_t ws_bytes, void* stream);
+                       const float* amax_in, float* alpha_out, uint8_t* codes_t,
+                       uint8_t* scales_t, uint8_t* choice_t, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* MXFP4 quantization (NVIDIA NVFP4 article sec. 1 and 5; AMD MI355X MXFP4
  * article sec. 2).  Per 32 values: optional 32-point Hadamard (FP4_HAD32,

@@ -86,9 +86,9 @@ def test_amax_rejects(L):
     assert L.fp4_tensor_amax(P, 32, 64, 0, 0, F4, P, 8, None) == E_WS
 
 
-def rq(L, codes=P, scales=P, alpha=F4, rows=32, cols=64, flags=0, alpha_out=F4, ct=P, st=P,
-       choice=None, ws=P, wsb=1 << 20):
-    return L.nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags, 0, alpha_out, ct, st,
+def rq(L, codes=P, scales=P, alpha=F4, rows=32, cols=64, flags=0, amax=None, alpha_out=F4, ct=P,
+       st=P, choice=None, ws=P, wsb=1 << 20):
+    return L.nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags, 0, amax, alpha_out, ct, st,
                                 choice, ws, wsb, None)
 
 
@@ -99,7 +99,7 @@ def test_requant_rejects(L):
     assert rq(L, alpha_out=None) == E_NULL
     assert rq(L, ct=None) == E_NULL
     assert rq(L, st=None) == E_NULL
-    assert rq(L, ws=None) == E_NULL
+    assert rq(L, ws=None) == E_NULL                         # amax computed -> needs workspace
     assert rq(L, rows=24) == E_SHAPE                        # rows % 16
     assert rq(L, cols=40) == E_SHAPE                        # cols % 16
     assert rq(L, rows=-16) == E_SHAPE
@@ -109,6 +109,7 @@ def test_requant_rejects(L):
     assert rq(L, codes=Q) == E_ALIGN
     assert rq(L, ct=Q) == E_ALIGN
     assert rq(L, alpha=F4 + 1) == E_ALIGN
+    assert rq(L, amax=F4 + 2) == E_ALIGN
     assert rq(L, wsb=16) == E_WS
 
 

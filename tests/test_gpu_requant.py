@@ -79,6 +79,24 @@ def test_requant_of_quantized_gradient(flags):
     run_case(codes, scales, alpha, flags, ctx="c4-gradient")
 
 
+@pytest.mark.parametrize("flags", [fp4.FOUR_OVER_SIX, fp4.RHT16 | fp4.SR])
+def test_requant_amax_given(flags):
+    """With the amax given, the result is the oracle's fp32 quantizer on the
+    dequantized transpose with that amax (here 1.5x the unrotated maximum)."""
+    codes, scales, alpha = quantized("c2", 272, 784)
+    rows, cols = 272, 784
+    xt = np.ascontiguousarray(O.dequantize(0, codes, scales, alpha, rows, cols).T)
+    amax = np.float32(1.5) * np.abs(xt).max()
+    print("requant amax given", flags, float(amax), flush=True)
+    got = fp4.nvfp4_requantize_t(u8(codes), u8(scales), f32(alpha), flags, seed=SEED,
+                                 amax=f32(amax), want_choice=True)
+    torch.cuda.synchronize()
+    want = O.nvfp4_quantize_f32(xt, flags, seed=SEED, amax=amax)
+    for k in ["codes", "scales"] + (["choice"] if flags & fp4.FOUR_OVER_SIX else []):
+        assert np.array_equal(got[k].cpu().numpy(), want[k]), k
+    assert got["alpha"].cpu().numpy()[0] == want["alpha"]
+
+
 def test_requant_edge_cases():
     # thin tensors: one block row / one block column
     for shape in ((16, 4096 + 16), (4096 + 16, 16), (16, 32)):
