@@ -66,11 +66,10 @@ __device__ __forceinline__ float2_t fp4x2_to_f32(uint32_t packed, float scale) {
 // Salmon, Moraes, Dror, Shaw (SC'11).  Returns output word 0 only; the
 // compiler drops the work the last rounds spend on the other words.
 // a ^ b ^ k in one VALU instruction: gfx950's three-input bitwise op with
-// truth table 0x96 (odd parity of the three bits).  k is a uniform value.
+// truth table 0x96 (odd parity of the three bits).  Through the compiler
+// builtin, not inline asm, so that no hazard padding follows it.
 __device__ __forceinline__ uint32_t xor3_vvs(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
 __device__ __forceinline__ uint32_t philox_w0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,

@@ -87,25 +87,28 @@ void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* al
                     uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t, uint64_t seed,
                     hipStream_t st) {
   const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
-  const int64_t tiles_x = cdiv(cols, kRqTileCols);
-  const int64_t ntiles = cdiv(rows, kRqTileRows) * tiles_x;
+  // grids are multiples of 8 (one equal share of the tiles per XCD) once
+  // there are 8 tiles
+  const uint32_t TY = (uint32_t)cdiv(rows, kRqTileRows), TX = (uint32_t)cdiv(cols, kRqTileCols);
+  const int64_t ntiles = (int64_t)TY * TX;
+  auto grid = [&](int64_t cap) {
+    int64_t g = ntiles < cap ? ntiles : cap;
+    if (g >= 8) g -= g % 8;
+    return g < 1 ? (int64_t)1 : g;
+  };
   const int64_t resident = (int64_t)num_cus() * kRqWgPerCu;
   const uint32_t* abits = (const uint32_t*)amax_in;
   int namax = 1;
   if (!amax_in) {
-    int64_t ga = ntiles < kRqAmaxGroups ? ntiles : kRqAmaxGroups;
-    if (ga > resident) ga = resident;
-    if (ga < 1) ga = 1;
-    rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols,
-                                                            tiles_x, ntiles, ws, lo, hi);
+    const int64_t ga = grid(resident < kRqAmaxGroups ? resident : kRqAmaxGroups);
+    rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols, TY,
+                                                            TX, ws, lo, hi);
     abits = ws;
     namax = (int)ga;
   }
-  int64_t gq = ntiles < resident ? ntiles : resident;
-  if (gq < 1) gq = 1;
-  rq_quant_kernel<F46, SR, RHT><<<(unsigned)gq, kRqThreads, 0, st>>>(
-      codes, scales, alpha, rows, cols, tiles_x, ntiles, abits, namax, alpha_out, codes_t,
-      scales_t, choice_t, lo, hi);
+  rq_quant_kernel<F46, SR, RHT><<<(unsigned)grid(resident), kRqThreads, 0, st>>>(
+      codes, scales, alpha, rows, cols, TY, TX, abits, namax, alpha_out,
+      codes_t, scales_t, choice_t, lo, hi);
 }
 
 }  // namespace

@@ -17,8 +17,14 @@
 // 8 columns -- so each of its 256 output rows gets one complete 128-byte
 // line of codes from one CU (no partial lines shared between L2s), and a
 // wave's loads read two 128-byte input row pieces per instruction.
-// Persistent workgroups stride over the tiles.  A first pass computes the
-// output's tensor amax (after RHT16 when asked) the same way.
+// Tiles are taken in super-tile-major order (8 x 8 super-tiles), and each
+// XCD takes one contiguous eighth of that order, its persistent workgroups
+// striding through it: the tiles of a super-tile run on one XCD at the same
+// time, so the eight tiles side by side that share each 128-byte line of
+// input scales, and the eight stacked tiles that share each line of output
+// scales, meet in one L2, while every XCD gets the same number of tiles.
+// A first pass computes the output's tensor amax (after RHT16 when asked)
+// the same way.
 #pragma once
 
 #include "device_common.h"
@@ -30,6 +36,7 @@ constexpr int kRqThreads = 512;
 constexpr int kRqTileRows = 256;   // 16 segments of 16 input rows
 constexpr int kRqTileCols = 256;   // 32 groups of 8 input columns
 constexpr int kRqWgPerCu = 2;
+constexpr int kRqSuper = 8;           // tiles per side of an XCD super-tile
 constexpr int kRqAmaxGroups = 1024;   // most partial maxima the amax pass writes
 
 // The 16 dequantized values of column pair B of the thread's 8 columns
@@ -57,6 +64,38 @@ __device__ __forceinline__ void rq_rotate(float* y, uint32_t signs) {
   }
 }
 
+// The j-th tile in super-tile-major order: kRqSuper x kRqSuper super-tiles
+// row by row, tiles row-major inside each (the last super-row and
+// super-column may be smaller).  Tile counts stay below 2^29.
+__device__ __forceinline__ TileOrder rq_tile(uint32_t j, uint32_t TY, uint32_t TX) {
+  const uint32_t sy = j / (kRqSuper * TX), r = j - sy * kRqSuper * TX;
+  const uint32_t h = min((uint32_t)kRqSuper, TY - kRqSuper * sy);
+  const uint32_t sx = r / (kRqSuper * h), within = r - sx * kRqSuper * h;
+  const uint32_t w = min((uint32_t)kRqSuper, TX - kRqSuper * sx);
+  const uint32_t wy = within / w;
+  TileOrder t;
+  t.ty = kRqSuper * sy + wy;
+  t.tx = kRqSuper * sx + (within - wy * w);
+  return t;
+}
+
+// This workgroup's tiles: j, j + step, ... below end.  With a grid that is
+// a multiple of 8, workgroup b runs on XCD b % 8 and that XCD owns tiles
+// [x n / 8, (x + 1) n / 8) of the order above; other grids share one range.
+struct RqRange {
+  uint32_t j, end, step;
+};
+
+__device__ __forceinline__ RqRange rq_range(uint32_t ntiles) {
+  const uint32_t nx = gridDim.x % kXcds == 0 ? kXcds : 1;
+  const uint32_t x = blockIdx.x % nx, k = blockIdx.x / nx;
+  RqRange q;
+  q.j = (uint32_t)((uint64_t)ntiles * x / nx) + k;
+  q.end = (uint32_t)((uint64_t)ntiles * (x + 1) / nx);
+  q.step = gridDim.x / nx;
+  return q;
+}
+
 // Where a thread's segment of a tile sits, and whether it is inside the
 // tensor (rows % 16 == 0 and cols % 16 == 0 make each segment of 16 rows x
 // 8 columns wholly inside or wholly outside).
@@ -65,12 +104,11 @@ struct RqSeg {
   bool in;
 };
 
-__device__ __forceinline__ RqSeg rq_seg(int64_t tile, int64_t tiles_x, int64_t rows, int64_t cols) {
+__device__ __forceinline__ RqSeg rq_seg(const TileOrder& to, int64_t rows, int64_t cols) {
   const int t = threadIdx.x, cg = t & 31, s = t >> 5;
-  const int64_t ty = tile / tiles_x, tx = tile - ty * tiles_x;
   RqSeg g;
-  g.r0 = ty * kRqTileRows + 16 * s;
-  g.c0 = tx * kRqTileCols + 8 * cg;
+  g.r0 = to.ty * kRqTileRows + 16 * s;
+  g.c0 = to.tx * kRqTileCols + 8 * cg;
   g.in = g.r0 < rows && g.c0 < cols;
   return g;
 }
@@ -95,15 +133,15 @@ __device__ __forceinline__ void rq_load(const uint8_t* __restrict__ codes,
 template <bool RHT>
 __global__ __launch_bounds__(kRqThreads) void rq_amax_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ alpha_in, int64_t rows, int64_t cols, int64_t tiles_x,
-    int64_t ntiles, uint32_t* __restrict__ partials, uint32_t seed_lo, uint32_t seed_hi) {
+    const float* __restrict__ alpha_in, int64_t rows, int64_t cols, uint32_t TY, uint32_t TX,
+    uint32_t* __restrict__ partials, uint32_t seed_lo, uint32_t seed_hi) {
   __shared__ uint32_t red[kRqThreads / 64];
   const float alpha = *alpha_in;
   uint32_t signs = 0;
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
   float m = 0.0f;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const RqSeg g = rq_seg(tile, tiles_x, rows, cols);
+  for (RqRange q = rq_range(TY * TX); q.j < q.end; q.j += q.step) {
+    const RqSeg g = rq_seg(rq_tile(q.j, TY, TX), rows, cols);
     if (!g.in) continue;
     uint32_t cw[16];
     float sc[16];
@@ -166,8 +204,8 @@ __device__ __forceinline__ void rq_block(const float* y, const float2* tab, floa
 template <bool FOUR_SIX, bool SR, bool RHT>
 __global__ __launch_bounds__(kRqThreads) void rq_quant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ alpha_in, int64_t rows, int64_t cols, int64_t tiles_x,
-    int64_t ntiles, const uint32_t* __restrict__ partials, int npart,
+    const float* __restrict__ alpha_in, int64_t rows, int64_t cols, uint32_t TY, uint32_t TX,
+    const uint32_t* __restrict__ partials, int npart,
     float* __restrict__ alpha_out, uint8_t* __restrict__ codes_t,
     uint8_t* __restrict__ scales_t, uint8_t* __restrict__ choice_t, uint32_t seed_lo,
     uint32_t seed_hi) {
@@ -184,8 +222,8 @@ __global__ __launch_bounds__(kRqThreads) void rq_quant_kernel(
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
   __syncthreads();
 
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const RqSeg g = rq_seg(tile, tiles_x, rows, cols);
+  for (RqRange q = rq_range(TY * TX); q.j < q.end; q.j += q.step) {
+    const RqSeg g = rq_seg(rq_tile(q.j, TY, TX), rows, cols);
     if (!g.in) continue;
     uint32_t cw[16];
     float sc[16];
