@@ -85,6 +85,8 @@ def lib():
         L.orc_mxfp4_quantize.restype = C.c_int
         L.orc_mxfp4_quantize.argtypes = [u16p, C.c_int64, C.c_int64, C.c_uint32,
                                          u8p, u8p, u8p, u8p, f32p, f32p]
+        L.orc_nvfp4_simulate.restype = C.c_int
+        L.orc_nvfp4_simulate.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int, C.c_float, f32p]
         L.orc_dequantize.restype = C.c_int
         L.orc_dequantize.argtypes = [C.c_int, u8p, u8p, C.c_float, C.c_int64, C.c_int64,
                                      C.c_uint32, f32p]
@@ -278,6 +280,22 @@ def mxfp4_quantize(x_bf16, flags=ROWWISE | COLWISE, debug=False):
         out.update(codes_c=cc, scales_c=sc)
     if debug:
         out.update(t_r=tr, t_c=tc)
+    return out
+
+
+SIM_NVFP4, SIM_SCALE_HP, SIM_VALUE_HP, SIM_THRESHOLD = 0, 1, 2, 3
+
+
+def nvfp4_simulate(x_bf16, mode=SIM_NVFP4, thr=0.0):
+    """RTN6 quantize-then-dequantize of x with one error source switched off
+    (the simulated quantization of the 4/6 paper's Fig. 2); fp32 [rows][cols]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    out = np.zeros((rows, cols), np.float32)
+    rc = lib().orc_nvfp4_simulate(_p(x, C.c_uint16), rows, cols, mode, C.c_float(thr),
+                                  _p(out, C.c_float))
+    if rc != 0:
+        raise ValueError("orc_nvfp4_simulate failed: %d" % rc)
     return out
 
 

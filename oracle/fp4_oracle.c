@@ -494,6 +494,53 @@ int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float al
 }
 
 /* ===================================================================== */
+/* Error study ([4/6] sec. 2.2, Fig. 2)                                    */
+/* ===================================================================== */
+
+/* [4/6] sec. 2.1 names two sources of NVFP4 error, the E4M3 rounding of the
+ * block scale and the FP4 rounding of the scaled values; sec. 2.2 (Fig. 2)
+ * removes one at a time, and then rounds only the scaled values below a
+ * threshold.  Each step below is the plain RTN6 quantizer of this file
+ * (Eq. 1-3 with the encode factors of R5) with the named rounding left
+ * out. */
+int orc_nvfp4_simulate(const uint16_t* x, int64_t rows, int64_t cols, int mode,
+                       float thr, float* out) {
+  if (rows < 0 || cols < 0 || cols % 16) return -1;
+  if (mode < ORC_SIM_NVFP4 || mode > ORC_SIM_THRESHOLD) return -1;
+  if (rows * cols > 0 && (!x || !out)) return -1;
+  float amax = 0.0f;
+  for (int64_t i = 0; i < rows * cols; i++) {
+    const float a = fabsf(bf16_to_f32(x[i]));
+    if (a > amax) amax = a;
+  }
+  const float alpha = amax / (6.0f * 448.0f);           /* Eq. 1, M = 6 only */
+  const float k6 = (amax == 0.0f) ? 0.0f : 448.0f / amax;
+  for (int64_t r = 0; r < rows; r++) {
+    for (int64_t c0 = 0; c0 < cols; c0 += 16) {
+      float y[16], amax_b = 0.0f;
+      for (int k = 0; k < 16; k++) {
+        y[k] = bf16_to_f32(x[r * cols + c0 + k]);
+        if (fabsf(y[k]) > amax_b) amax_b = fabsf(y[k]);
+      }
+      const float dpre = amax_b * k6;                    /* Eq. 2, unrounded */
+      const float delta = (mode == ORC_SIM_SCALE_HP) ? dpre
+                                                     : orc_e4m3_decode(orc_e4m3_encode(dpre));
+      const float s = alpha * delta;
+      const float rcp = (s == 0.0f) ? 0.0f : 1.0f / s;
+      for (int k = 0; k < 16; k++) {
+        const float t = y[k] * rcp;                      /* scaled value     */
+        int round_it = 1;
+        if (mode == ORC_SIM_VALUE_HP) round_it = 0;
+        if (mode == ORC_SIM_THRESHOLD) round_it = fabsf(t) < thr;
+        const float q = round_it ? orc_e2m1_decode(orc_e2m1_encode(t)) : t;
+        out[r * cols + c0 + k] = q * s;
+      }
+    }
+  }
+  return 0;
+}
+
+/* ===================================================================== */
 /* MXFP4 ([NVFP4] sec. 1 and 5; [MXFP4] sec. 2)                           */
 /* ===================================================================== */
 

@@ -98,9 +98,6 @@ int orc_mxfp4_quantize(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                        uint8_t* codes_c, uint8_t* scales_c,
                        float* t_r, float* t_c);
 
-/* Dequantization. format 0 = NVFP4 (alpha used, BLOCK2D selects 16x16
- * tiles), 1 = MXFP4 (row-wise layout; pass the transposed shape for the
- * column-wise outputs). */
 /* NVFP4 quantization of an fp32 tensor (1D flags only: RTN6, FOUR_OVER_SIX,
  * SR, RHT16); the same definition as orc_nvfp4_quantize on fp32 values. */
 int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -117,9 +114,30 @@ int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float al
                            float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
                            uint8_t* choice_t);
 
+/* Dequantization. format 0 = NVFP4 (alpha used, BLOCK2D selects 16x16
+ * tiles), 1 = MXFP4 (row-wise layout; pass the transposed shape for the
+ * column-wise outputs). */
 int orc_dequantize(int format, const uint8_t* codes, const uint8_t* scales,
                    float alpha, int64_t rows, int64_t cols, uint32_t flags,
                    float* out);
+
+/* Simulated NVFP4 for the error study of [4/6] sec. 2.2 (Fig. 2): the 1D
+ * RTN6 quantize-then-dequantize of x [rows][cols] (bf16, cols % 16 == 0)
+ * into out (fp32), with one source of error switched off:
+ *   ORC_SIM_NVFP4      nothing switched off: out = dequantize(quantize(x))
+ *   ORC_SIM_SCALE_HP   the block scale is not rounded to E4M3 (Delta kept
+ *                      in fp32)
+ *   ORC_SIM_VALUE_HP   the scaled values X/(alpha Delta) are not rounded
+ *                      to FP4 (kept in fp32)
+ *   ORC_SIM_THRESHOLD  a scaled value t is rounded to FP4 only when
+ *                      |t| < thr; the others are kept in fp32
+ * Returns 0, or -1 for a bad shape or mode. */
+#define ORC_SIM_NVFP4     0
+#define ORC_SIM_SCALE_HP  1
+#define ORC_SIM_VALUE_HP  2
+#define ORC_SIM_THRESHOLD 3
+int orc_nvfp4_simulate(const uint16_t* x_bf16, int64_t rows, int64_t cols, int mode,
+                       float thr, float* out);
 
 #ifdef __cplusplus
 }
