@@ -79,6 +79,9 @@ def lib():
         L.orc_nvfp4_quantize_f32.restype = C.c_int
         L.orc_nvfp4_quantize_f32.argtypes = [f32p, C.c_int64, C.c_int64, C.c_uint32, C.c_uint64,
                                              f32p, f32p, u8p, u8p, u8p]
+        L.orc_nvfp4_quantize_rows.restype = C.c_int
+        L.orc_nvfp4_quantize_rows.argtypes = [u16p, C.c_int64, C.c_int64, C.c_uint32, C.c_uint64,
+                                              f32p, u8p, u8p, u8p]
         L.orc_nvfp4_requantize_t.restype = C.c_int
         L.orc_nvfp4_requantize_t.argtypes = [u8p, u8p, C.c_float, C.c_int64, C.c_int64,
                                              C.c_uint32, C.c_uint64, f32p, u8p, u8p, u8p]
@@ -233,6 +236,23 @@ def nvfp4_quantize_f32(x_f32, flags=0, seed=0, amax=None):
     if rc != 0:
         raise ValueError("oracle nvfp4_quantize_f32 rejected the arguments (%d)" % rc)
     return dict(codes=codes, scales=scales, alpha=np.float32(alpha[0]), choice=choice)
+
+
+def nvfp4_quantize_rows(x_bf16, flags=0, seed=0):
+    """NVFP4 with one FP32 scale per row (1D flags); dict(codes, scales,
+    alpha [rows], choice)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    choice = np.zeros((rows, cols // 16), np.uint8)
+    alpha = np.zeros(max(rows, 1), np.float32)
+    rc = lib().orc_nvfp4_quantize_rows(
+        _p(x, C.c_uint16), rows, cols, flags, C.c_uint64(seed & (2**64 - 1)), _p(alpha, C.c_float),
+        _p(codes, C.c_uint8), _p(scales, C.c_uint8), _p(choice, C.c_uint8))
+    if rc != 0:
+        raise ValueError("orc_nvfp4_quantize_rows failed: %d" % rc)
+    return {"codes": codes, "scales": scales, "alpha": alpha[:rows], "choice": choice}
 
 
 def nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags=0, seed=0):

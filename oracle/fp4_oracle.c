@@ -347,11 +347,32 @@ static block_result quantize_block(float* const* elems, int n, float amax_b,
 }
 
 /* NVFP4 quantization of x (bf16) or, when x is NULL, of xf (fp32). */
+/* Tensor-level constants from an amax: Eq. 1 and the encode factors. */
+typedef struct {
+  float alpha, k6, k4;
+} scale_consts;
+
+static scale_consts consts_from_amax(float amax, int four_six) {
+  /* Eq. 1: alpha = amax / (M_FP4 * M_FP8).  Reading: the scale maximum is
+   * C = 448 for the 6-only path and C = 256 when 4/6 is on, so that the
+   * M = 4 block scale (amax_b * 6*256/(4*amax) <= 384) stays in E4M3 range. */
+  const float C = four_six ? 256.0f : 448.0f;
+  scale_consts sc;
+  sc.alpha = amax / (6.0f * C);
+  /* Encode factors k_M = (6*C/M) / amax, i.e. 1/(alpha*M) taken directly
+   * from amax ([NVFP4] sec. 6: global encode scale 6*448/amax). */
+  sc.k6 = (amax == 0.0f) ? 0.0f : C / amax;
+  sc.k4 = (amax == 0.0f) ? 0.0f : (1.5f * C) / amax;
+  return sc;
+}
+
+/* rowscale != 0: every row takes its own constants from its own amax
+ * (alpha_out then holds one value per row); 1D only. */
 static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, int64_t cols,
                               uint32_t flags, uint64_t seed, const float* amax_in,
                               float* alpha_out, uint8_t* codes, uint8_t* scales,
                               uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
-                              orc_debug* dbg) {
+                              orc_debug* dbg, int rowscale) {
   if (!nvfp4_flags_ok(rows, cols, flags)) return -1;
   if (!codes || !scales || !alpha_out) return -2;
   const int two_d = (flags & ORC_BLOCK2D) != 0;
@@ -361,26 +382,18 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
   float* y = load_rotated(x, xf, rows, cols, flags, seed);
   if (!y) return -3;
 
-  /* Eq. 1: alpha = amax / (M_FP4 * M_FP8).  Reading: the scale maximum is
-   * C = 448 for the 6-only path and C = 256 when 4/6 is on, so that the
-   * M = 4 block scale (amax_b * 6*256/(4*amax) <= 384) stays in E4M3 range. */
-  float amax;
+  if (rowscale && (two_d || amax_in)) { free(y); return -1; }
+  float amax = 0.0f;
   if (amax_in) {
     amax = *amax_in;
-  } else {
-    amax = 0.0f;
+  } else if (!rowscale) {
     for (int64_t i = 0; i < rows * cols; i++) {
       const float a = fabsf(y[i]);
       if (a > amax) amax = a;
     }
   }
-  const float C = four_six ? 256.0f : 448.0f;
-  const float alpha = amax / (6.0f * C);
-  *alpha_out = alpha;
-  /* Per-tensor encode factors k_M = (6*C/M) / amax, i.e. 1/(alpha*M) taken
-   * directly from amax ([NVFP4] sec. 6: global encode scale 6*448/amax). */
-  const float k6 = (amax == 0.0f) ? 0.0f : C / amax;
-  const float k4 = (amax == 0.0f) ? 0.0f : (1.5f * C) / amax;
+  scale_consts sc = consts_from_amax(amax, four_six);
+  if (!rowscale) *alpha_out = sc.alpha;
 
   const int64_t bcols = cols / 16;                        /* blocks per row */
   const int64_t brows = two_d ? rows / 16 : rows;         /* block rows     */
@@ -394,6 +407,15 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
   float t6[256], t4[256], u6[256], p6[256];
 
   for (int64_t br = 0; br < brows; br++) {
+    if (rowscale) {                      /* this row's own amax and constants */
+      float amax_r = 0.0f;
+      for (int64_t c = 0; c < cols; c++) {
+        const float a = fabsf(y[br * cols + c]);
+        if (a > amax_r) amax_r = a;
+      }
+      sc = consts_from_amax(amax_r, four_six);
+      alpha_out[br] = sc.alpha;
+    }
     for (int64_t bc = 0; bc < bcols; bc++) {
       /* gather the block, row by row */
       float amax_b = 0.0f;
@@ -405,7 +427,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
         const float a = fabsf(*elems[i]);
         if (a > amax_b) amax_b = a;
       }
-      block_result res6 = quantize_block(elems, bn, amax_b, alpha, k6, flags, seed, idx,
+      block_result res6 = quantize_block(elems, bn, amax_b, sc.alpha, sc.k6, flags, seed, idx,
                                          c6, t6, u6, p6);
       block_result chosen = res6;
       const uint8_t* cc = c6;
@@ -413,7 +435,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
       int pick4 = 0;
       block_result res4 = res6;
       if (four_six) {
-        res4 = quantize_block(elems, bn, amax_b, alpha, k4, flags, seed, idx, c4, t4,
+        res4 = quantize_block(elems, bn, amax_b, sc.alpha, sc.k4, flags, seed, idx, c4, t4,
                               NULL, NULL);
         /* [4/6] sec. 1: keep the candidate with the smaller error; ties keep
          * M = 6. */
@@ -451,7 +473,7 @@ int orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                        orc_debug* dbg) {
   if (!x && rows * cols > 0) return -2;
   return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, amax_in, alpha_out, codes,
-                            scales, choice, codes_t, scales_t, dbg);
+                            scales, choice, codes_t, scales_t, dbg, 0);
 }
 
 int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -460,7 +482,22 @@ int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t 
   if (!x && rows * cols > 0) return -2;
   if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
   return nvfp4_quantize_any(NULL, x, rows, cols, flags, seed, amax_in, alpha_out, codes,
-                            scales, choice, NULL, NULL, NULL);
+                            scales, choice, NULL, NULL, NULL, 0);
+}
+
+/* NVFP4 with one FP32 scale per row instead of per tensor: the finer
+ * global scale [NVFP4] sec. 9 proposes so that the quantizer needs no
+ * separate pass over memory for the amax.  Row r is quantized exactly as
+ * the per-tensor quantizer would, with alpha_r = amax_r / (6 C) from the
+ * row's own largest magnitude (after RHT16 when asked); the SR counter stays
+ * the element index in the whole tensor. */
+int orc_nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                            uint64_t seed, float* alpha_rows, uint8_t* codes,
+                            uint8_t* scales, uint8_t* choice) {
+  if (!x && rows * cols > 0) return -2;
+  if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
+  return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, NULL, alpha_rows, codes, scales,
+                            choice, NULL, NULL, NULL, 1);
 }
 
 /* Requantization for the transposed operand of the backward pass ([QII]
@@ -486,7 +523,7 @@ int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float al
     for (int64_t r = 0; r < rows; r++)
       for (int64_t c = 0; c < cols; c++) xt[c * rows + r] = xd[r * cols + c];
     rc = nvfp4_quantize_any(NULL, xt, cols, rows, flags, seed, NULL, alpha_out, codes_t,
-                            scales_t, choice_t, NULL, NULL, NULL);
+                            scales_t, choice_t, NULL, NULL, NULL, 0);
   }
   free(xd);
   free(xt);

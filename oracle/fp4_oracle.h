@@ -104,6 +104,13 @@ int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t 
                            uint64_t seed, const float* amax_in, float* alpha_out,
                            uint8_t* codes, uint8_t* scales, uint8_t* choice);
 
+/* NVFP4 (1D flags) with one FP32 scale per row: row r uses alpha_r =
+ * amax_r / (6 C) from its own largest magnitude (after RHT16); alpha_rows
+ * [rows].  Otherwise identical to orc_nvfp4_quantize. */
+int orc_nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                            uint32_t flags, uint64_t seed, float* alpha_rows,
+                            uint8_t* codes, uint8_t* scales, uint8_t* choice);
+
 /* Requantize a 1D NVFP4 tensor X [rows][cols] (codes, scales, alpha) for the
  * transposed operand: NVFP4 (flags as above) of dequantize(X)^T, giving
  * codes_t [cols][rows/2], scales_t [cols][rows/16], choice_t (or NULL).
