@@ -41,6 +41,7 @@ KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c3": "nvfp4_2d_kernel<true, true>",
              "c4": "nvfp4_1d_kernel<false, true, true>",
              "c5": "mxfp4_kernel<true, true, true>",
+             "f2": "nvfp4_rows_wg_kernel<true, false, false, 1, true>",
              "f4a": "rq_quant_kernel<true, false, true>",
              "f4g": "rq_quant_kernel<false, true, true>"}
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
@@ -53,11 +54,15 @@ ROWS = {
     "c3": (14336, 4096, "nvfp4", 1 | 8 | 64, "nvfp4_2d16x16_four_over_six_transposed_14336x4096"),
     "c4": (8192, 14336, "nvfp4", 2 | 4, "nvfp4_rht16_sr_8192x14336"),
     "c5": (16384, 8192, "mxfp4", 16 | 32 | 64, "mxfp4_had32_row_col_16384x8192"),
+    # one FP32 scale per row instead of per tensor: quantized in one read
+    "f2": (8192, 4096, "rows", 1, "nvfp4_rowscale_four_over_six_8192x4096"),
     # requantization of a 1D NVFP4 tensor for the transposed operand; the
     # input is the activation (4/6) or the gradient (RHT16 + SR) quantized
     "f4a": (8192, 4096, "requant", 1 | 4, "nvfp4_requant_t_rht16_four_over_six_8192x4096"),
     "f4g": (8192, 14336, "requant", 2 | 4, "nvfp4_requant_t_rht16_sr_8192x14336"),
 }
+# workload -> the seeded tensor it quantizes, where that is another workload's
+DATA_OF = {"f2": "c2"}
 # requant workload -> (workload whose quantization is the input, its flags)
 REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
 SEED = 0x0123456789ABCDEF
@@ -68,6 +73,8 @@ def algorithmic_bytes(wl):
     n = rows * cols
     if kind == "requant":                            # NVFP4 in, NVFP4 of the transpose out
         return 2 * (n // 2 + n // 16 + 4)
+    if kind == "rows":                               # one fp32 scale per row
+        return 2 * n + n // 2 + n // 16 + 4 * rows
     if kind == "mxfp4":
         return 2 * n + 2 * (n // 2 + n // 32)
     if flags & 8:                                    # 16x16 tiles
@@ -116,14 +123,19 @@ class Row:
         if kind == "requant":
             self._init_requant(fp4, torch, synthetic, np, dev)
             return
-        x_np = synthetic.gen(wl)
+        x_np = synthetic.gen(DATA_OF.get(wl, wl))
         self.x_np = x_np
         x0 = torch.from_numpy(x_np.view(np.int16)).to(dev)
         nbytes = x0.numel() * 2
         self.nbuf = min(64, max(4, -(-(1 << 30) // nbytes)))   # >= 1 GiB of inputs (c1: 64 copies)
         self.xs = [x0] + [x0.clone() for _ in range(self.nbuf - 1)]
         self.outs = []
-        if kind == "nvfp4":
+        if kind == "rows":
+            for _ in range(self.nbuf):
+                self.outs.append(dict(codes=torch.empty((rows, cols // 2), dtype=u8, device=dev),
+                                      scales=torch.empty((rows, cols // 16), dtype=u8, device=dev),
+                                      alpha=torch.empty(rows, dtype=torch.float32, device=dev)))
+        elif kind == "nvfp4":
             two_d = bool(flags & 8)
             srows = rows // 16 if two_d else rows
             for _ in range(self.nbuf):
@@ -153,7 +165,12 @@ class Row:
         self.args_step, self.args_kernel = [], []
         for k in range(self.nbuf):
             o, xp = self.outs[k], self.xs[k].data_ptr()
-            if kind == "nvfp4":
+            if kind == "rows":              # a single kernel: step and kernel are one call
+                a = (xp, rows, cols, flags, SEED, o["alpha"].data_ptr(), o["codes"].data_ptr(),
+                     o["scales"].data_ptr(), None, self.sp)
+                self.args_step.append(a)
+                self.args_kernel.append(a)
+            elif kind == "nvfp4":
                 ct = o["codes_t"].data_ptr() if "codes_t" in o else None
                 st = o["scales_t"].data_ptr() if "scales_t" in o else None
                 common = (xp, rows, cols, flags, SEED)
@@ -168,7 +185,8 @@ class Row:
                      o["codes_c"].data_ptr(), o["scales_c"].data_ptr(), self.sp)
                 self.args_step.append(a)
                 self.args_kernel.append(a)
-        self.fn = L.nvfp4_quantize if kind == "nvfp4" else L.mxfp4_quantize
+        self.fn = {"nvfp4": L.nvfp4_quantize, "rows": L.nvfp4_quantize_rows,
+                   "mxfp4": L.mxfp4_quantize}[kind]
         torch.cuda.synchronize()
 
     def _init_requant(self, fp4, torch, synthetic, np, dev):
@@ -273,6 +291,8 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
         t0 = time.perf_counter()
         if kind == "nvfp4":
             oracle.nvfp4_quantize(x, flags, seed=SEED)
+        elif kind == "rows":
+            oracle.nvfp4_quantize_rows(x, flags, seed=SEED)
         elif kind == "requant":
             oracle.nvfp4_requantize_t(q["codes"], q["scales"], q["alpha"], x.shape[0], cols, flags,
                                       seed=SEED)
@@ -422,7 +442,7 @@ def main():
     }
     if not args.no_rows:
         rows = []
-        for wl in ("c1", "c3", "c4", "c5", "f4a", "f4g"):
+        for wl in ("c1", "c3", "c4", "c5", "f2", "f4a", "f4g"):
             r = Row(wl, fp4, torch, synthetic, np)
             st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
             kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)

@@ -32,8 +32,9 @@ FORMAT_MXFP4 = 1
 STATUS = {0: "FP4_OK", -1: "FP4_E_NULL", -2: "FP4_E_SHAPE", -3: "FP4_E_ALIGN",
           -4: "FP4_E_FLAGS", -5: "FP4_E_WORKSPACE", -6: "FP4_E_HIP"}
 
-EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_requantize_t",
-           "mxfp4_quantize", "fp4_dequantize", "fp4_status_str", "fp4_abi_version")
+EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_quantize_rows",
+           "nvfp4_requantize_t", "mxfp4_quantize", "fp4_dequantize", "fp4_status_str",
+           "fp4_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4q.so")
@@ -62,6 +63,8 @@ def lib():
         L.fp4_tensor_amax.argtypes = [vp, i64, i64, u32, u64, vp, vp, sz, vp]
         L.nvfp4_quantize.restype = C.c_int
         L.nvfp4_quantize.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.nvfp4_quantize_rows.restype = C.c_int
+        L.nvfp4_quantize_rows.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp]
         L.nvfp4_requantize_t.restype = C.c_int
         L.nvfp4_requantize_t.argtypes = [vp, vp, vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, sz,
                                          vp]
@@ -169,6 +172,27 @@ def nvfp4_quantize(x, flags=0, seed=0, amax=None, want_choice=False, ws=None, st
         o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o.get("choice")),
         _ptr(o.get("codes_t")), _ptr(o.get("scales_t")), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return o
+
+
+def nvfp4_quantize_rows(x, flags=0, seed=0, want_choice=False, stream=None, out=None):
+    """NVFP4 with one FP32 scale per row, in one read of x.  Returns a dict
+    with ``codes`` [rows][cols/2], ``scales`` [rows][cols/16], ``alpha``
+    [rows] (float32) and, when asked, ``choice``."""
+    torch = _torch()
+    xb = _as_bits(x)
+    rows, cols = xb.shape
+    dev = x.device
+    o = dict(out or {})
+    u8 = torch.uint8
+    o.setdefault("codes", torch.empty((rows, cols // 2), dtype=u8, device=dev))
+    o.setdefault("scales", torch.empty((rows, cols // 16), dtype=u8, device=dev))
+    o.setdefault("alpha", torch.empty(max(rows, 1), dtype=torch.float32, device=dev))
+    if want_choice:
+        o.setdefault("choice", torch.empty((rows, cols // 16), dtype=u8, device=dev))
+    _check("nvfp4_quantize_rows", lib().nvfp4_quantize_rows(
+        xb.data_ptr(), rows, cols, flags, seed & (2**64 - 1), o["alpha"].data_ptr(),
+        o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o.get("choice")), _stream(stream)))
     return o
 
 

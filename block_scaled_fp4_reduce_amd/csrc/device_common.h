@@ -211,6 +211,44 @@ __host__ __device__ inline int64_t xcd_grid(int64_t TY, int64_t TX, int SY, int 
   return ((NS + kXcds - 1) / kXcds) * kXcds * (int64_t)SY * SX;
 }
 
+// Cross-lane reads inside a 16-lane DPP row (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
+
+// Max over the 16 lanes of a DPP row, in every lane of the row (the xor-1,
+// xor-2, half-mirror and mirror steps pair the lanes as a butterfly would).
+__device__ __forceinline__ float tile_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+
+// Max of a non-negative value over the whole (fully active) wave, as a
+// uniform value: DPP max inside each 16-lane row, then the four row results
+// through readlane (for non-negative floats the bit patterns order as the
+// values do).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  const uint32_t t = __float_as_uint(tile_max(v));
+  const uint32_t a = __builtin_amdgcn_readlane(t, 0), b = __builtin_amdgcn_readlane(t, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(t, 32), d = __builtin_amdgcn_readlane(t, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return __uint_as_float(ab > cd ? ab : cd);
+}
+
+// Order LDS traffic of one wave (its lanes exchange data through LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------- wave/workgroup max
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 #pragma unroll

@@ -7,6 +7,7 @@
 #include "nvfp4_2d_kernels.h"
 #include "nvfp4_kernels.h"
 #include "requant_kernels.h"
+#include "rows_kernels.h"
 
 using namespace fp4q;
 
@@ -109,6 +110,67 @@ void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* al
   rq_quant_kernel<F46, SR, RHT><<<(unsigned)grid(resident), kRqThreads, 0, st>>>(
       codes, scales, alpha, rows, cols, TY, TX, abits, namax, alpha_out,
       codes_t, scales_t, choice_t, lo, hi);
+}
+
+// Persistent grid: as many workgroups of `kernel` as fit on the chip at
+// once (its register use sets that; queried once per kernel), at most
+// `want`.
+int64_t resident_grid(const void* kernel, int& per_cu, int64_t want) {
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kRowThreads, 0) != hipSuccess ||
+        n < 1)
+      n = 2;
+    per_cu = n < kRowWgPerCu ? n : kRowWgPerCu;
+  }
+  const int64_t cap = (int64_t)num_cus() * per_cu;
+  int64_t g = want < cap ? want : cap;
+  return g < 1 ? 1 : g;
+}
+
+template <bool F46, bool SR, bool RHT, int NB>
+void launch_rows_wave(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                      uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                      hipStream_t st) {
+  static int per_cu = 0;
+  const int64_t grid = resident_grid((const void*)nvfp4_rows_kernel<F46, SR, RHT, NB>, per_cu,
+                                     cdiv(rows, kRowWaves));
+  nvfp4_rows_kernel<F46, SR, RHT, NB><<<(unsigned)grid, kRowThreads, 0, st>>>(
+      x, rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+template <bool F46, bool SR, bool RHT, int NB, bool ONE>
+void launch_rows_wg(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                    uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                    hipStream_t st) {
+  static int per_cu = 0;
+  const int64_t grid =
+      resident_grid((const void*)nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, per_cu, rows);
+  nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE><<<(unsigned)grid, kRowThreads, 0, st>>>(
+      x, rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// Rows of up to 128 blocks: one wave per row (1 or 2 blocks per lane).
+// Longer rows: one workgroup per row, 1, 2 or 4 blocks per thread held in
+// registers (rows up to 16384 values are read once); beyond that two
+// sweeps over the row, the second from cache.
+template <bool F46, bool SR, bool RHT>
+void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                 uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                 hipStream_t st) {
+  const int64_t nblk = cols / 16;
+  if (nblk <= 64)
+    launch_rows_wave<F46, SR, RHT, 1>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+  else if (nblk <= 128)
+    launch_rows_wave<F46, SR, RHT, 2>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+  else if (nblk <= 256)
+    launch_rows_wg<F46, SR, RHT, 1, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+  else if (nblk <= 512)
+    launch_rows_wg<F46, SR, RHT, 2, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+  else if (nblk <= 1024)
+    launch_rows_wg<F46, SR, RHT, 4, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+  else
+    launch_rows_wg<F46, SR, RHT, 4, false>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
 }
 
 }  // namespace
@@ -234,6 +296,31 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float*
   else if (rht) FP4Q_RQ(false, false, true);
   else FP4Q_RQ(false, false, false);
 #undef FP4Q_RQ
+  return launched();
+}
+
+int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                        uint64_t seed, float* alpha_rows, uint8_t* codes, uint8_t* scales,
+                        uint8_t* choice, void* stream) {
+  const int64_t n = rows * cols;
+  if (n > 0 && (!x || !alpha_rows || !codes || !scales)) return FP4_E_NULL;
+  if (int rc = check_shape(rows, cols)) return rc;
+  if (cols % 16) return FP4_E_SHAPE;
+  if (flags & ~(uint32_t)(FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16)) return FP4_E_FLAGS;
+  if (int rc = check_nvfp4_flags(flags)) return rc;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(alpha_rows, 4)) return FP4_E_ALIGN;
+  if (n == 0) return FP4_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
+#define FP4Q_ROWS(F, S, R) \
+  launch_rows<F, S, R>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st)
+  if (f46 && rht) FP4Q_ROWS(true, false, true);
+  else if (f46) FP4Q_ROWS(true, false, false);
+  else if (sr && rht) FP4Q_ROWS(false, true, true);
+  else if (sr) FP4Q_ROWS(false, true, false);
+  else if (rht) FP4Q_ROWS(false, false, true);
+  else FP4Q_ROWS(false, false, false);
+#undef FP4Q_ROWS
   return launched();
 }
 

@@ -39,40 +39,16 @@ struct Strips {   // one lane's tile row in each of the k2dStrips strips
   uint4 v[2 * k2dStrips];
 };
 
-// Cross-lane reads inside a 16-lane DPP row (no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
-constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
-
-// Max / sum over the 16 lanes of a tile, same bits in every lane.  After
-// the xor-1 and xor-2 steps every group of 4 lanes holds one value, after
-// the half-row mirror every group of 8, so the mirrors pair exactly the
-// groups an xor-4 / xor-8 butterfly would: the sum is the pairwise tree
+// Sum over the 16 lanes of a tile, same bits in every lane.  After the
+// xor-1 and xor-2 steps every group of 4 lanes holds one value, after the
+// half-row mirror every group of 8, so the mirrors pair exactly the groups
+// an xor-4 / xor-8 butterfly would: the sum is the pairwise tree
 // ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)) + (same for 8..15).
-__device__ __forceinline__ float tile_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  return fmaxf(v, dpp_f<kDppMirror>(v));
-}
-
 __device__ __forceinline__ float tile_sum(float v) {
   v = v + dpp_f<kDppXor1>(v);
   v = v + dpp_f<kDppXor2>(v);
   v = v + dpp_f<kDppHalfMirror>(v);
   return v + dpp_f<kDppMirror>(v);
-}
-
-// Order LDS traffic of one wave (its lanes exchange data through LDS).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <bool FOUR_SIX, bool TRANSPOSE>

@@ -245,6 +245,74 @@ __device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t& ca, uint32
 #endif
 }
 
+// One quantized 16-value block: its two code words, E4M3 scale code and
+// 4/6 choice (1 where M = 4 won).
+struct BlockOut {
+  uint32_t w0, w1, scale, pick4;
+};
+
+// Quantize the 16-value block y whose first element has index idx in its
+// row-major tensor (the SR counter), with the (s, 1/s) table and encode
+// factors of its scale.
+// The block's largest magnitude, max |y_k| from +0.
+__device__ __forceinline__ float block_amax16(const float* y) {
+  float amax_b = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k++) amax_b = fmaxf(amax_b, fabsf(y[k]));
+  return amax_b;
+}
+
+// quant_block with the block's amax (block_amax16(y)) already known.
+template <bool FOUR_SIX, bool SR>
+__device__ __forceinline__ BlockOut quant_block_m(const float* y, float amax_b, const float2* tab,
+                                                  float k6, float k4, int64_t idx,
+                                                  uint32_t seed_lo, uint32_t seed_hi) {
+  uint32_t e6, e4;
+  e4m3_pair(amax_b * k6, amax_b * k4, e6, e4);
+  const float2 sr6 = tab[e6];
+  BlockOut o;
+  o.w0 = __builtin_nondeterministic_value(0u);
+  o.w1 = __builtin_nondeterministic_value(0u);
+  o.scale = e6;
+  o.pick4 = 0;
+  if constexpr (SR) {
+    quant16_sr(y, sr6.x, sr6.y, (uint64_t)idx, seed_lo, seed_hi, o.w0, o.w1);
+  } else {
+    const float err6 = quant16_rtn(y, sr6.x, sr6.y, o.w0, o.w1);
+    if constexpr (FOUR_SIX) {
+      const float2 sr4 = tab[e4];
+      uint32_t u0 = __builtin_nondeterministic_value(0u), u1 = __builtin_nondeterministic_value(0u);
+      const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
+      o.pick4 = err4 < err6 ? 1u : 0u;    // ties keep M = 6
+      o.w0 = o.pick4 ? u0 : o.w0;
+      o.w1 = o.pick4 ? u1 : o.w1;
+      o.scale = o.pick4 ? e4 : e6;
+    }
+  }
+  return o;
+}
+
+template <bool FOUR_SIX, bool SR>
+__device__ __forceinline__ BlockOut quant_block(const float* y, const float2* tab, float k6,
+                                                float k4, int64_t idx, uint32_t seed_lo,
+                                                uint32_t seed_hi) {
+  return quant_block_m<FOUR_SIX, SR>(y, block_amax16(y), tab, k6, k4, idx, seed_lo, seed_hi);
+}
+
+// quant_block, stored for a 1D block layout: codes at idx / 2, scale and
+// choice at idx / 16.
+template <bool FOUR_SIX, bool SR>
+__device__ __forceinline__ void quant_block_at(const float* y, const float2* tab, float k6,
+                                               float k4, int64_t idx, uint32_t seed_lo,
+                                               uint32_t seed_hi, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ scales,
+                                               uint8_t* __restrict__ choice) {
+  const BlockOut o = quant_block<FOUR_SIX, SR>(y, tab, k6, k4, idx, seed_lo, seed_hi);
+  *(uint2*)(codes + idx / 2) = make_uint2(o.w0, o.w1);
+  scales[idx / 16] = (uint8_t)o.scale;
+  if (choice) choice[idx / 16] = (uint8_t)o.pick4;
+}
+
 // Quantize the lane's 16-value block (raw bf16 in v0, v1) and store codes,
 // scale and choice at byte offsets 8*lane / lane / lane of the chunk's
 // output resources.

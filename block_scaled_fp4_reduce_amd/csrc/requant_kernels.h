@@ -164,42 +164,6 @@ __global__ __launch_bounds__(kRqThreads) void rq_amax_kernel(
   if (threadIdx.x == 0) partials[blockIdx.x] = mb;
 }
 
-// Quantize one output block y (output row orow, first output column ocol)
-// and store its 8 code bytes, scale and choice.
-template <bool FOUR_SIX, bool SR>
-__device__ __forceinline__ void rq_block(const float* y, const float2* tab, float k6, float k4,
-                                         int64_t orow, int64_t ocol, int64_t rows, uint32_t seed_lo,
-                                         uint32_t seed_hi, uint8_t* __restrict__ codes_t,
-                                         uint8_t* __restrict__ scales_t,
-                                         uint8_t* __restrict__ choice_t) {
-  float amax_b = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 16; k++) amax_b = fmaxf(amax_b, fabsf(y[k]));
-  uint32_t e6, e4;
-  e4m3_pair(amax_b * k6, amax_b * k4, e6, e4);
-  const float2 sr6 = tab[e6];
-  uint32_t w0 = __builtin_nondeterministic_value(0u), w1 = __builtin_nondeterministic_value(0u);
-  uint32_t scale = e6, pick4 = 0;
-  if constexpr (SR) {
-    quant16_sr(y, sr6.x, sr6.y, (uint64_t)(orow * rows + ocol), seed_lo, seed_hi, w0, w1);
-  } else {
-    const float err6 = quant16_rtn(y, sr6.x, sr6.y, w0, w1);
-    if constexpr (FOUR_SIX) {
-      const float2 sr4 = tab[e4];
-      uint32_t u0 = __builtin_nondeterministic_value(0u), u1 = __builtin_nondeterministic_value(0u);
-      const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
-      pick4 = err4 < err6 ? 1u : 0u;      // ties keep M = 6
-      w0 = pick4 ? u0 : w0;
-      w1 = pick4 ? u1 : w1;
-      scale = pick4 ? e4 : e6;
-    }
-  }
-  *(uint2*)(codes_t + orow * (rows / 2) + ocol / 2) = make_uint2(w0, w1);
-  const int64_t si = orow * (rows / 16) + ocol / 16;
-  scales_t[si] = (uint8_t)scale;
-  if (choice_t) choice_t[si] = (uint8_t)pick4;
-}
-
 // Pass 2: quantize with the tensor scale from the partial maxima.
 template <bool FOUR_SIX, bool SR, bool RHT>
 __global__ __launch_bounds__(kRqThreads) void rq_quant_kernel(
@@ -235,10 +199,11 @@ __global__ __launch_bounds__(kRqThreads) void rq_quant_kernel(
       rq_column_pair<B>(cw, sc, ya, yb);
       rq_rotate<RHT>(ya, signs);
       rq_rotate<RHT>(yb, signs);
-      rq_block<FOUR_SIX, SR>(ya, tab, ts.k6, ts.k4, g.c0 + 2 * B, g.r0, rows, seed_lo, seed_hi,
-                             codes_t, scales_t, choice_t);
-      rq_block<FOUR_SIX, SR>(yb, tab, ts.k6, ts.k4, g.c0 + 2 * B + 1, g.r0, rows, seed_lo,
-                             seed_hi, codes_t, scales_t, choice_t);
+      // element index in the output: output row g.c0 + j, column g.r0
+      quant_block_at<FOUR_SIX, SR>(ya, tab, ts.k6, ts.k4, (g.c0 + 2 * B) * rows + g.r0, seed_lo,
+                                   seed_hi, codes_t, scales_t, choice_t);
+      quant_block_at<FOUR_SIX, SR>(yb, tab, ts.k6, ts.k4, (g.c0 + 2 * B + 1) * rows + g.r0,
+                                   seed_lo, seed_hi, codes_t, scales_t, choice_t);
     };
     pair(std::integral_constant<int, 0>{});
     pair(std::integral_constant<int, 1>{});

@@ -118,6 +118,26 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                    uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* NVFP4 with one FP32 scale per row, quantized in a single read of x.  The
+ * NVIDIA NVFP4 article (sec. 9) names the extra memory pass for the global
+ * scale as a cost and proposes finer-grained global scales, per row or per
+ * block.  Row r takes alpha_r = amax_r / (6*C) ("Four Over Six" Eq. 1 on
+ * the row; C = 448, or 256 with FOUR_OVER_SIX; amax after RHT16 when asked)
+ * and is otherwise quantized exactly as nvfp4_quantize would quantize it
+ * (Eq. 2-3, 4/6, SR with counter = row*cols + col).  Results differ from
+ * nvfp4_quantize wherever rows have different maxima; a consumer decodes
+ * row r with alpha_rows[r].
+ *   flags      FP4_RTN6 or FOUR_OVER_SIX, SR, RHT16 (SR|FOUR_OVER_SIX
+ *              rejected); BLOCK2D, COLWISE, ROWWISE and HAD32 rejected.
+ *   alpha_rows [rows] device floats.
+ *   codes      [rows][cols/2];  scales [rows][cols/16];  choice NULL or
+ *              [rows][cols/16].
+ *   Shapes: cols % 16 == 0.  No workspace. */
+int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols,
+                        uint32_t flags, uint64_t seed, float* alpha_rows,
+                        uint8_t* codes, uint8_t* scales, uint8_t* choice,
+                        void* stream);
+
 /* Requantization of a 1D NVFP4 tensor for the transposed operand: the
  * NVFP4 quantization of dequantize(X)^T, with its own tensor scale.  The
  * backward pass quantizes data a second time (Quartet II / MS-EDEN

@@ -113,6 +113,23 @@ def test_requant_rejects(L):
     assert rq(L, wsb=16) == E_WS
 
 
+def test_rows_rejects(L):
+    def rows(x=P, r=32, c=64, flags=0, alpha=F4, codes=P, scales=P):
+        return L.nvfp4_quantize_rows(x, r, c, flags, 0, alpha, codes, scales, None, None)
+    assert rows(x=None) == E_NULL
+    assert rows(alpha=None) == E_NULL
+    assert rows(codes=None) == E_NULL
+    assert rows(scales=None) == E_NULL
+    assert rows(c=40) == E_SHAPE
+    assert rows(r=-1) == E_SHAPE
+    for f in (fp4.BLOCK2D, fp4.COLWISE, fp4.HAD32, fp4.SR | fp4.FOUR_OVER_SIX, 1 << 9):
+        assert rows(flags=f) == E_FLAGS, f
+    assert rows(x=P + 2) == E_ALIGN
+    assert rows(codes=Q) == E_ALIGN
+    assert rows(alpha=F4 + 1) == E_ALIGN
+    assert L.nvfp4_quantize_rows(None, 0, 64, 0, 0, None, None, None, None, None) == OK
+
+
 def test_mx_rejects(L):
     f = fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE
     assert L.mxfp4_quantize(None, 64, 64, f, P, P, P, P, None) == E_NULL
