@@ -27,6 +27,7 @@ BLOCK2D = 1 << 3
 HAD32 = 1 << 4
 ROWWISE = 1 << 5
 COLWISE = 1 << 6
+MSEDEN = 1 << 7
 
 _CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", "-Wall", "-Wextra"]

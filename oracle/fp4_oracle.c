@@ -228,7 +228,10 @@ static float* load_rotated(const uint16_t* x, const float* xf, int64_t rows, int
 
 static int nvfp4_flags_ok(int64_t rows, int64_t cols, uint32_t flags) {
   if (rows < 0 || cols < 0) return 0;
-  if (flags & ~(ORC_FOUR_OVER_SIX | ORC_SR | ORC_RHT16 | ORC_BLOCK2D | ORC_ROWWISE | ORC_COLWISE)) return 0;
+  if (flags & ~(ORC_FOUR_OVER_SIX | ORC_SR | ORC_RHT16 | ORC_BLOCK2D | ORC_ROWWISE | ORC_COLWISE |
+                ORC_MSEDEN)) return 0;
+  if ((flags & ORC_MSEDEN) &&
+      (!(flags & ORC_RHT16) || (flags & (ORC_SR | ORC_FOUR_OVER_SIX | ORC_BLOCK2D)))) return 0;
   if ((flags & ORC_SR) && (flags & ORC_FOUR_OVER_SIX)) return 0;
   if ((flags & ORC_BLOCK2D) && (flags & (ORC_SR | ORC_RHT16))) return 0;
   if ((flags & ORC_COLWISE) && !(flags & ORC_BLOCK2D)) return 0;
@@ -347,6 +350,70 @@ static block_result quantize_block(float* const* elems, int n, float amax_b,
 }
 
 /* NVFP4 quantization of x (bf16) or, when x is NULL, of xf (fp32). */
+/* Stochastic rounding of a block scale d >= 0 (in E4M3 units) onto the E4M3
+ * grid: between neighbouring E4M3 values lo <= d < hi it rounds up with
+ * probability p = (d - lo)/(hi - lo) (exact: the spacing is a power of two),
+ * using u = (Philox word 0 >> 8) * 2^-24 for key = seed and counter =
+ * (block index lo, block index hi, 1, 0), up iff u < p; d >= 448 gives 448.
+ * Returns the E4M3 code. */
+static uint8_t e4m3_sr(float d, uint64_t seed, uint64_t blk, float* u_out) {
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  const uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 1u, 0u};
+  uint32_t w[4];
+  orc_philox4x32_10(ctr, key, w);
+  const float u = (float)(w[0] >> 8) * 0x1p-24f;
+  if (u_out) *u_out = u;
+  if (!(d > 0.0f)) return 0;
+  if (d >= 448.0f) return 0x7E;
+  int e2;
+  frexp((double)d, &e2);
+  int E = e2 - 1;
+  if (E < -6) E = -6;                          /* subnormals share 2^-6's step */
+  const double quantum = ldexp(1.0, E - 3);
+  double n = floor((double)d / quantum);       /* lo = n * quantum            */
+  const double p = ((double)d - n * quantum) / quantum;
+  if ((double)u < p) n += 1.0;
+  long code = ((long)(E + 7) << 3) + (long)n - 8;
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)code;
+}
+
+/* One MS-EDEN block (reading R26 of the design notes, after [QII] sec. 1:
+ * rotation, round-to-nearest FP4 values, randomness only in the 8-bit
+ * scale; the unbiasing factor is EDEN's, Vargaftik et al. 2022):
+ *   Delta_pre = amax_b * k6 (Eq. 2, unrounded), s = fl(alpha * Delta_pre),
+ *   t_k = y_k * fl(1/s), q_k = nearest E2M1 to t_k (saturating),
+ *   N = sum t_k^2, D = sum t_k * q_k (each two fma chains over elements
+ *   0..7 and 8..15, added), S = N / D (1 when D = 0),
+ *   Delta' = fl(S * Delta_pre), scale = E4M3 code of SR(Delta').
+ * y holds the 16 rotated values; codes_out gets the 16 codes. */
+static uint8_t quantize_block_msed(const float* y, float amax_b, float alpha, float k6,
+                                   uint64_t seed, uint64_t blk, uint8_t* codes_out,
+                                   float* dprime_out) {
+  const float dpre = amax_b * k6;
+  const float s = alpha * dpre;
+  const float r = (s == 0.0f) ? 0.0f : 1.0f / s;
+  float t[16];
+  for (int k = 0; k < 16; k++) {
+    t[k] = y[k] * r;
+    codes_out[k] = orc_e2m1_encode(t[k]);
+  }
+  float n_lo = 0.0f, n_hi = 0.0f, d_lo = 0.0f, d_hi = 0.0f;
+  for (int k = 0; k < 8; k++) {
+    n_lo = fmaf(t[k], t[k], n_lo);
+    d_lo = fmaf(t[k], orc_e2m1_decode(codes_out[k]), d_lo);
+  }
+  for (int k = 8; k < 16; k++) {
+    n_hi = fmaf(t[k], t[k], n_hi);
+    d_hi = fmaf(t[k], orc_e2m1_decode(codes_out[k]), d_hi);
+  }
+  const float N = n_lo + n_hi, D = d_lo + d_hi;
+  const float S = (D > 0.0f) ? N / D : 1.0f;
+  const float dprime = S * dpre;
+  if (dprime_out) *dprime_out = dprime;
+  return e4m3_sr(dprime, seed, blk, NULL);
+}
+
 /* Tensor-level constants from an amax: Eq. 1 and the encode factors. */
 typedef struct {
   float alpha, k6, k4;
@@ -377,6 +444,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
   if (!codes || !scales || !alpha_out) return -2;
   const int two_d = (flags & ORC_BLOCK2D) != 0;
   const int four_six = (flags & ORC_FOUR_OVER_SIX) != 0;
+  const int msed = (flags & ORC_MSEDEN) != 0;
   if (two_d && (flags & ORC_COLWISE) && (!codes_t || !scales_t)) return -2;
 
   float* y = load_rotated(x, xf, rows, cols, flags, seed);
@@ -392,7 +460,9 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
       if (a > amax) amax = a;
     }
   }
-  scale_consts sc = consts_from_amax(amax, four_six);
+  /* MS-EDEN takes C = 256 like 4/6: its corrected scale may exceed the
+   * block's unrounded one (by at most ~1.22), and 448/256 leaves room */
+  scale_consts sc = consts_from_amax(amax, four_six || msed);
   if (!rowscale) *alpha_out = sc.alpha;
 
   const int64_t bcols = cols / 16;                        /* blocks per row */
@@ -413,7 +483,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
         const float a = fabsf(y[br * cols + c]);
         if (a > amax_r) amax_r = a;
       }
-      sc = consts_from_amax(amax_r, four_six);
+      sc = consts_from_amax(amax_r, four_six || msed);
       alpha_out[br] = sc.alpha;
     }
     for (int64_t bc = 0; bc < bcols; bc++) {
@@ -426,6 +496,16 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
         idx[i] = (uint64_t)(r * cols + c);
         const float a = fabsf(*elems[i]);
         if (a > amax_b) amax_b = a;
+      }
+      if (msed) {                      /* 1D only (flags checked above) */
+        float yb[16];
+        for (int i = 0; i < 16; i++) yb[i] = *elems[i];
+        const int64_t bidx = br * bcols + bc;
+        scales[bidx] = quantize_block_msed(yb, amax_b, sc.alpha, sc.k6, seed, (uint64_t)bidx,
+                                           c6, dbg && dbg->dpre6 ? &dbg->dpre6[bidx] : NULL);
+        if (choice) choice[bidx] = 0;
+        for (int i = 0; i < 16; i++) put_nibble(&codes[br * (cols / 2)], bc * 16 + i, c6[i]);
+        continue;
       }
       block_result res6 = quantize_block(elems, bn, amax_b, sc.alpha, sc.k6, flags, seed, idx,
                                          c6, t6, u6, p6);

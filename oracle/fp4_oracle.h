@@ -44,6 +44,7 @@ extern "C" {
 #define ORC_HAD32         (1u << 4)
 #define ORC_ROWWISE       (1u << 5)
 #define ORC_COLWISE       (1u << 6)
+#define ORC_MSEDEN        (1u << 7)   /* NVFP4: RTN values, stochastic E4M3 scale (needs RHT16) */
 
 /* ---- number formats ---- */
 uint8_t orc_e2m1_encode(float t);                /* 4-bit code, RNE, saturating */
@@ -69,7 +70,8 @@ typedef struct {
   float* u;        /* SR uniform in [0,1) (SR only)                          */
   float* p;        /* SR round-up probability (SR only)                      */
   /* optional per-block outputs, one per block (layout of `scales`)         */
-  float* dpre6;    /* unrounded block scale for M = 6                        */
+  float* dpre6;    /* unrounded block scale for M = 6; with MSEDEN the
+                      corrected scale Delta' that is stochastically rounded */
   float* dpre4;    /* unrounded block scale for M = 4 (4/6 only)            */
   float* err6;     /* block squared error, M = 6 (4/6 only)                  */
   float* err4;     /* block squared error, M = 4 (4/6 only)                  */
