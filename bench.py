@@ -41,6 +41,7 @@ KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c3": "nvfp4_2d_kernel<true, true>",
              "c4": "nvfp4_1d_kernel<false, true, true>",
              "c5": "mxfp4_kernel<true, true, true>",
+             "f1": "nvfp4_msed_kernel<true>",
              "f2": "nvfp4_rows_wg_kernel<true, false, false, 1, true>",
              "f4a": "rq_quant_kernel<true, false, true>",
              "f4g": "rq_quant_kernel<false, true, true>"}
@@ -54,6 +55,8 @@ ROWS = {
     "c3": (14336, 4096, "nvfp4", 1 | 8 | 64, "nvfp4_2d16x16_four_over_six_transposed_14336x4096"),
     "c4": (8192, 14336, "nvfp4", 2 | 4, "nvfp4_rht16_sr_8192x14336"),
     "c5": (16384, 8192, "mxfp4", 16 | 32 | 64, "mxfp4_had32_row_col_16384x8192"),
+    # MS-EDEN on the gradient: RTN values, stochastic E4M3 scale
+    "f1": (8192, 14336, "nvfp4", 4 | 128, "nvfp4_msed_rht16_8192x14336"),
     # one FP32 scale per row instead of per tensor: quantized in one read
     "f2": (8192, 4096, "rows", 1, "nvfp4_rowscale_four_over_six_8192x4096"),
     # requantization of a 1D NVFP4 tensor for the transposed operand; the
@@ -62,7 +65,7 @@ ROWS = {
     "f4g": (8192, 14336, "requant", 2 | 4, "nvfp4_requant_t_rht16_sr_8192x14336"),
 }
 # workload -> the seeded tensor it quantizes, where that is another workload's
-DATA_OF = {"f2": "c2"}
+DATA_OF = {"f1": "c4", "f2": "c2"}
 # requant workload -> (workload whose quantization is the input, its flags)
 REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
 SEED = 0x0123456789ABCDEF
@@ -446,7 +449,7 @@ def main():
     }
     if not args.no_rows:
         rows = []
-        for wl in ("c1", "c3", "c4", "c5", "f2", "f4a", "f4g"):
+        for wl in ("c1", "c3", "c4", "c5", "f1", "f2", "f4a", "f4g"):
             r = Row(wl, fp4, torch, synthetic, np)
             st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
             kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)

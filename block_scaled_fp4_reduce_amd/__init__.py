@@ -24,6 +24,7 @@ BLOCK2D = 1 << 3
 HAD32 = 1 << 4
 ROWWISE = 1 << 5
 COLWISE = 1 << 6
+MSEDEN = 1 << 7
 RTN6 = 0
 
 FORMAT_NVFP4 = 0

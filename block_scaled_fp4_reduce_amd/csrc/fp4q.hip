@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/fp4q.h"
+#include "msed_kernels.h"
 #include "mx_kernels.h"
 #include "nvfp4_2d_kernels.h"
 #include "nvfp4_kernels.h"
@@ -14,8 +15,8 @@ using namespace fp4q;
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
-constexpr uint32_t kNvfp4Flags =
-    FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16 | FP4_BLOCK2D | FP4_ROWWISE | FP4_COLWISE;
+constexpr uint32_t kNvfp4Flags = FP4_FOUR_OVER_SIX | FP4_SR | FP4_RHT16 | FP4_BLOCK2D |
+                                 FP4_ROWWISE | FP4_COLWISE | FP4_MSEDEN;
 constexpr uint32_t kMxFlags = FP4_HAD32 | FP4_ROWWISE | FP4_COLWISE;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -34,6 +35,9 @@ int check_nvfp4_flags(uint32_t flags) {
   if ((flags & FP4_SR) && (flags & FP4_FOUR_OVER_SIX)) return FP4_E_FLAGS;
   if ((flags & FP4_BLOCK2D) && (flags & (FP4_SR | FP4_RHT16))) return FP4_E_FLAGS;
   if ((flags & FP4_COLWISE) && !(flags & FP4_BLOCK2D)) return FP4_E_FLAGS;
+  if ((flags & FP4_MSEDEN) &&
+      (!(flags & FP4_RHT16) || (flags & (FP4_SR | FP4_FOUR_OVER_SIX | FP4_BLOCK2D))))
+    return FP4_E_FLAGS;
   return FP4_OK;
 }
 
@@ -249,6 +253,14 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
     const bool f46 = (flags & FP4_FOUR_OVER_SIX) != 0;
     launch_nvfp4_2d(x, rows, cols, f46, abits, namax, alpha_out, codes, scales, choice,
                     want_t ? codes_t : nullptr, want_t ? scales_t : nullptr, st, num_cus());
+    return launched();
+  }
+  if (flags & FP4_MSEDEN) {              // always with RHT16 (checked above)
+    int64_t grid = nblocks > 0 ? cdiv(nblocks, (int64_t)kThreads) : 1;
+    if (grid > (int64_t)num_cus() * kWgPerCu) grid = (int64_t)num_cus() * kWgPerCu;
+    nvfp4_msed_kernel<true><<<(unsigned)grid, kThreads, 0, st>>>(
+        (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
+        (uint32_t)seed, (uint32_t)(seed >> 32));
     return launched();
   }
   const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;

@@ -70,8 +70,10 @@ enum {
   FP4_BLOCK2D = 1u << 3,       /* NVFP4: 16x16 tiles instead of 1x16 blocks   */
   FP4_HAD32 = 1u << 4,         /* MXFP4: 32-point Hadamard before quantizing  */
   FP4_ROWWISE = 1u << 5,       /* MXFP4: emit row-wise output                 */
-  FP4_COLWISE = 1u << 6        /* MXFP4: emit column-wise output;
+  FP4_COLWISE = 1u << 6,       /* MXFP4: emit column-wise output;
                                   NVFP4 2D: also emit the transpose          */
+  FP4_MSEDEN = 1u << 7         /* NVFP4: MS-EDEN -- RTN values, unbiasing
+                                  factor, stochastic E4M3 scale (with RHT16) */
 };
 
 enum { FP4_FORMAT_NVFP4 = 0, FP4_FORMAT_MXFP4 = 1 };
@@ -98,8 +100,17 @@ int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols,
 /* NVFP4 quantization ("Four Over Six" Eq. 1-3 and sec. 1; NVIDIA NVFP4
  * article sec. 2 and sec. 6).
  *   flags     FP4_RTN6 or any of FOUR_OVER_SIX, SR, RHT16, BLOCK2D
- *             (+ COLWISE with BLOCK2D).  Rejected: SR|FOUR_OVER_SIX,
- *             BLOCK2D|SR, BLOCK2D|RHT16, HAD32, COLWISE without BLOCK2D.
+ *             (+ COLWISE with BLOCK2D), or MSEDEN|RHT16.  Rejected:
+ *             SR|FOUR_OVER_SIX, BLOCK2D|SR, BLOCK2D|RHT16, HAD32, COLWISE
+ *             without BLOCK2D, MSEDEN without RHT16 or with SR,
+ *             FOUR_OVER_SIX or BLOCK2D.
+ *             MSEDEN (Quartet II / MS-EDEN article, sec. 1: rotation,
+ *             round-to-nearest values, randomness only in the 8-bit scale;
+ *             the unbiasing factor is EDEN's): per block the values are
+ *             rounded to nearest against the unrounded scale Delta_pre,
+ *             the scale becomes S * Delta_pre with S = sum t^2 / sum t q
+ *             and is rounded stochastically to E4M3 (Philox counter =
+ *             (block index lo, hi, 1, 0)); C = 256.
  *   seed      Philox key for SR (counter = row*cols + col) and RHT16 signs.
  *   amax_in   NULL: computed here (one extra read of x, needs `ws`);
  *             else one device float taken as the tensor's largest magnitude.

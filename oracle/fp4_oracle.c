@@ -19,6 +19,17 @@
  *   2D tiles ............................ pinned (transpose identity)
  *   MXFP4 ............................... pinned (power-of-two scales,
  *                                         scaled block max in [4, 8), hand cases)
+ *   requantization for the transpose .... pinned (equals the bf16 path when
+ *                                         the dequantized values are bf16-exact)
+ *   one scale per row ................... pinned (each row = the per-tensor
+ *                                         quantizer on that row alone)
+ *   error-study simulation .............. pinned (no switch = dequantize of
+ *                                         the quantizer, sweep end points)
+ *   MS-EDEN ............................. partly pinned: the unbiasing factor
+ *                                         is not on the pages (EDEN's is taken);
+ *                                         its projection property, nearest
+ *                                         values, scale-rounding statistics,
+ *                                         removed scale bias, error vs SR
  *   exact fp32 operation order of the 4/6 error sum, the SR word-to-uniform
  *   mapping and the RHT sign source are choices where the pages are silent;
  *   they are fixed here and pinned only by the properties above.

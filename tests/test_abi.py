@@ -69,6 +69,9 @@ def test_nvfp4_rejects(L):
     assert nvq(L, flags=fp4.HAD32) == E_FLAGS
     assert nvq(L, flags=fp4.COLWISE) == E_FLAGS            # transposed output needs 2D
     assert nvq(L, flags=1 << 9) == E_FLAGS
+    assert nvq(L, flags=fp4.MSEDEN) == E_FLAGS                 # MS-EDEN needs RHT16
+    for f in (fp4.SR, fp4.FOUR_OVER_SIX, fp4.BLOCK2D):
+        assert nvq(L, flags=fp4.MSEDEN | fp4.RHT16 | f) == E_FLAGS
     assert nvq(L, x=P + 2) == E_ALIGN
     assert nvq(L, codes=Q) == E_ALIGN
     assert nvq(L, alpha=F4 + 1) == E_ALIGN

@@ -59,7 +59,7 @@ def run_case(x, flags, seed=SEED, amax_in=False):
 
 
 FLAG_SETS = [0, fp4.FOUR_OVER_SIX, fp4.SR, fp4.RHT16, fp4.RHT16 | fp4.SR,
-             fp4.RHT16 | fp4.FOUR_OVER_SIX]
+             fp4.RHT16 | fp4.FOUR_OVER_SIX, fp4.RHT16 | fp4.MSEDEN]
 
 
 @pytest.mark.parametrize("flags", FLAG_SETS)
@@ -69,7 +69,8 @@ def test_parity_small(wl, shape, flags):
     run_case(S.gen(wl, *shape), flags)
 
 
-@pytest.mark.parametrize("flags", [0, fp4.FOUR_OVER_SIX, fp4.SR, fp4.RHT16 | fp4.SR])
+@pytest.mark.parametrize("flags", [0, fp4.FOUR_OVER_SIX, fp4.SR, fp4.RHT16 | fp4.SR,
+                                   fp4.RHT16 | fp4.MSEDEN])
 def test_parity_special_values(flags):
     run_case(S.special_values_tensor(48, 272), flags)
 
@@ -94,6 +95,12 @@ def test_parity_c2_full():
 def test_parity_c4_full():
     x = S.gen("c4")
     got, want = run_case(x, fp4.RHT16 | fp4.SR)
+
+
+def test_parity_c4_full_msed():
+    """MS-EDEN on the full gradient: RTN values against the unrounded scale,
+    EDEN's factor and one stochastic scale draw per block, bit for bit."""
+    run_case(S.gen("c4"), fp4.RHT16 | fp4.MSEDEN)
 
 
 def test_parity_workloads_at_other_sizes():
