@@ -331,6 +331,19 @@ def dequantize(fmt, codes, scales, alpha, rows, cols, flags=0):
     return out
 
 
+def mxfp4_gemm(a_codes, a_scales, bt_codes, bt_scales, M, N, K):
+    """C = A B for MXFP4 operands, the consumer of the quantized tensors
+    (NVIDIA NVFP4 article sec. 1 and 5: MXFP4 values with a power-of-two
+    scale per 32; the block-scaled matrix product is the next step of the
+    path).  A is [M][K] row-wise (codes [M][K/2], scales [M][K/32]); B is
+    given as its transpose [N][K] in the same layout (the column-wise output
+    of the MXFP4 quantizer).  The dequantized values are exact in fp32; the
+    product is a float64 matmul.  Returns float64 [M][N]."""
+    A = dequantize(1, a_codes, a_scales, 0.0, M, K).astype(np.float64)
+    BT = dequantize(1, bt_codes, bt_scales, 0.0, N, K).astype(np.float64)
+    return A @ BT.T
+
+
 def unpack_codes(packed):
     """[r][n/2] bytes -> [r][n] 4-bit codes (low nibble = even element)."""
     p = np.asarray(packed, np.uint8)
