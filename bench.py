@@ -43,6 +43,7 @@ KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c5": "mxfp4_kernel<true, true, true>",
              "f1": "nvfp4_msed_kernel<true>",
              "f2": "nvfp4_rows_wg_kernel<true, false, false, 1, true>",
+             "f3": "mxfp4_gemm_kernel",
              "f4a": "rq_quant_kernel<true, false, true>",
              "f4g": "rq_quant_kernel<false, true, true>"}
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
@@ -59,13 +60,18 @@ ROWS = {
     "f1": (8192, 14336, "nvfp4", 4 | 128, "nvfp4_msed_rht16_8192x14336"),
     # one FP32 scale per row instead of per tensor: quantized in one read
     "f2": (8192, 4096, "rows", 1, "nvfp4_rowscale_four_over_six_8192x4096"),
+    # the consumer: MXFP4 product of the 16384x8192 tensor's row-wise output
+    # (M x K) with a second 8192x8192 tensor's (as B^T, N x K)
+    "f3": (16384, 8192, "gemm", 16 | 32, "mxfp4_gemm_16384x8192x8192"),
     # requantization of a 1D NVFP4 tensor for the transposed operand; the
     # input is the activation (4/6) or the gradient (RHT16 + SR) quantized
     "f4a": (8192, 4096, "requant", 1 | 4, "nvfp4_requant_t_rht16_four_over_six_8192x4096"),
     "f4g": (8192, 14336, "requant", 2 | 4, "nvfp4_requant_t_rht16_sr_8192x14336"),
 }
 # workload -> the seeded tensor it quantizes, where that is another workload's
-DATA_OF = {"f1": "c4", "f2": "c2"}
+DATA_OF = {"f1": "c4", "f2": "c2", "f3": "c5"}
+GEMM_N = 8192                                   # f3: B^T rows (N); K = the tensor's cols
+MFMA_FP4_PEAK_TFLOPS = 10100.0                  # dense FP4 matrix peak of MI355X
 # requant workload -> (workload whose quantization is the input, its flags)
 REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
 SEED = 0x0123456789ABCDEF
@@ -74,6 +80,9 @@ SEED = 0x0123456789ABCDEF
 def algorithmic_bytes(wl):
     rows, cols, kind, flags, _ = ROWS[wl]
     n = rows * cols
+    if kind == "gemm":                               # operands in, fp32 C out
+        return rows * cols // 2 + rows * cols // 32 + 2 * (GEMM_N * cols // 2 + GEMM_N * cols // 32) \
+            + 4 * rows * GEMM_N
     if kind == "requant":                            # NVFP4 in, NVFP4 of the transpose out
         return 2 * (n // 2 + n // 16 + 4)
     if kind == "rows":                               # one fp32 scale per row
@@ -129,6 +138,9 @@ class Row:
         u8 = torch.uint8
         if kind == "requant":
             self._init_requant(fp4, torch, synthetic, np, dev)
+            return
+        if kind == "gemm":
+            self._init_gemm(fp4, torch, synthetic, np, dev)
             return
         x_np = synthetic.gen(DATA_OF.get(wl, wl))
         self.x_np = x_np
@@ -194,6 +206,24 @@ class Row:
                 self.args_kernel.append(a)
         self.fn = {"nvfp4": L.nvfp4_quantize, "rows": L.nvfp4_quantize_rows,
                    "mxfp4": L.mxfp4_quantize}[kind]
+        torch.cuda.synchronize()
+
+    def _init_gemm(self, fp4, torch, synthetic, np, dev):
+        """A = row-wise MXFP4 of the tensor [rows][cols]; B^T = row-wise MXFP4
+        of a second seeded tensor [GEMM_N][cols]; both made by the library."""
+        rows, cols = self.rows, self.cols
+        self.x_np = synthetic.gen(DATA_OF[self.wl])
+        qa = fp4.mxfp4_quantize(torch.from_numpy(self.x_np.view(np.int16)).to(dev), self.flags)
+        w = synthetic.gen(DATA_OF[self.wl], GEMM_N, cols, seed=4242)
+        qb = fp4.mxfp4_quantize(torch.from_numpy(w.view(np.int16)).to(dev), self.flags)
+        self.w_np = w
+        self.nbuf = 1
+        self.qa, self.qb = qa, qb
+        self.c = torch.empty((rows, GEMM_N), dtype=torch.float32, device=dev)
+        a = (qa["codes_r"].data_ptr(), qa["scales_r"].data_ptr(), qb["codes_r"].data_ptr(),
+             qb["scales_r"].data_ptr(), rows, GEMM_N, cols, self.c.data_ptr(), self.sp)
+        self.args_step, self.args_kernel = [a], [a]
+        self.fn = self.L.mxfp4_gemm
         torch.cuda.synchronize()
 
     def _init_requant(self, fp4, torch, synthetic, np, dev):
@@ -282,7 +312,7 @@ def copy_reference(torch, row):
 
 
 # ------------------------------------------------------------------ CPU side
-def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
+def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0, w_np=None):
     """The CPU oracle, as it stands (single-threaded C), on the workload or
     on its first max_rows rows; repeated until ~budget_s of work."""
     import numpy as np
@@ -295,6 +325,9 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
     while len(times) < 5 and (time.time() < t_end or len(times) < 1):
         if kind == "requant" and not times:                  # the input, made by the oracle
             q = oracle.nvfp4_quantize(x, REQUANT_SRC[wl][1], seed=SEED)
+        if kind == "gemm" and not times:                     # operands, made by the oracle
+            qa = oracle.mxfp4_quantize(x, flags)
+            qb = oracle.mxfp4_quantize(np.ascontiguousarray(w_np[:GEMM_N]), flags)
         t0 = time.perf_counter()
         if kind == "nvfp4":
             oracle.nvfp4_quantize(x, flags, seed=SEED)
@@ -303,12 +336,20 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0):
         elif kind == "requant":
             oracle.nvfp4_requantize_t(q["codes"], q["scales"], q["alpha"], x.shape[0], cols, flags,
                                       seed=SEED)
+        elif kind == "gemm":
+            oracle.mxfp4_gemm(qa["codes_r"], qa["scales_r"], qb["codes_r"], qb["scales_r"],
+                              x.shape[0], GEMM_N, cols)
         else:
             oracle.mxfp4_quantize(x, flags)
         times.append(time.perf_counter() - t0)
     times.sort()
     med = times[len(times) // 2]
     frac = x.shape[0] / rows
+    if kind == "gemm":
+        tfl = 2.0 * x.shape[0] * GEMM_N * cols / med / 1e12
+        return {"value": round(tfl, 5), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                "sample": "first %d of %d rows of A (numpy float64 matmul after the C "
+                          "dequantize), %d runs, median %.2f s" % (x.shape[0], rows, len(times), med)}
     gbs = algorithmic_bytes(wl) * frac / med / 1e9
     what = "full %dx%d workload" % (rows, cols) if max_rows is None else \
         "first %d of %d rows" % (x.shape[0], rows)
@@ -449,10 +490,21 @@ def main():
     }
     if not args.no_rows:
         rows = []
-        for wl in ("c1", "c3", "c4", "c5", "f1", "f2", "f4a", "f4g"):
+        for wl in ("c1", "c3", "c4", "c5", "f1", "f2", "f3", "f4a", "f4g"):
             r = Row(wl, fp4, torch, synthetic, np)
             st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
             kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)
+            if r.kind == "gemm":
+                fl = 2.0 * r.rows * GEMM_N * r.cols
+                entry = {"workload": r.label, "flops": fl, "kernel_us": round(kt * 1e3, 3),
+                         "tflops": round(fl / (kt * 1e-3) / 1e12, 1),
+                         "kernel_frac_mfma_fp4": round(fl / (kt * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4)}
+                if not args.no_cpu:
+                    entry["cpu_oracle"] = cpu_oracle(wl, r.x_np, max_rows=32, budget_s=3.0, w_np=r.w_np)
+                rows.append(entry)
+                del r
+                torch.cuda.empty_cache()
+                continue
             a = algorithmic_bytes(wl)
             entry = {"workload": r.label, "algorithmic_bytes": a,
                      "step_us": round(st * 1e3, 3), "step_gbs": round(a / (st * 1e-3) / 1e9, 1),

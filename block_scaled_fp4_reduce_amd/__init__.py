@@ -34,8 +34,8 @@ STATUS = {0: "FP4_OK", -1: "FP4_E_NULL", -2: "FP4_E_SHAPE", -3: "FP4_E_ALIGN",
           -4: "FP4_E_FLAGS", -5: "FP4_E_WORKSPACE", -6: "FP4_E_HIP"}
 
 EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_quantize_rows",
-           "nvfp4_requantize_t", "mxfp4_quantize", "fp4_dequantize", "fp4_status_str",
-           "fp4_abi_version")
+           "nvfp4_requantize_t", "mxfp4_quantize", "mxfp4_gemm", "fp4_dequantize",
+           "fp4_status_str", "fp4_abi_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp4q.so")
@@ -71,6 +71,8 @@ def lib():
                                          vp]
         L.mxfp4_quantize.restype = C.c_int
         L.mxfp4_quantize.argtypes = [vp, i64, i64, u32, vp, vp, vp, vp, vp]
+        L.mxfp4_gemm.restype = C.c_int
+        L.mxfp4_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp]
         L.fp4_dequantize.restype = C.c_int
         L.fp4_dequantize.argtypes = [C.c_int, vp, vp, vp, i64, i64, u32, vp, vp]
         L.fp4_status_str.restype = C.c_char_p
@@ -250,6 +252,23 @@ def mxfp4_quantize(x, flags=HAD32 | ROWWISE | COLWISE, stream=None, out=None):
         xb.data_ptr(), rows, cols, flags, _ptr(o.get("codes_r")), _ptr(o.get("scales_r")),
         _ptr(o.get("codes_c")), _ptr(o.get("scales_c")), _stream(stream)))
     return o
+
+
+def mxfp4_gemm(a_codes, a_scales, bt_codes, bt_scales, out=None, stream=None):
+    """C = A B (fp32 [M][N]) from row-wise MXFP4 A (codes [M][K/2], scales
+    [M][K/32]) and B^T in the same layout (codes [N][K/2], scales [N][K/32])."""
+    torch = _torch()
+    M, N, K = a_codes.shape[0], bt_codes.shape[0], a_codes.shape[1] * 2
+    if bt_codes.shape[1] * 2 != K:
+        raise ValueError("A and B^T disagree on K")
+    for t in (a_codes, a_scales, bt_codes, bt_scales):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous uint8 GPU tensors")
+    out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device) if out is None else out
+    _check("mxfp4_gemm", lib().mxfp4_gemm(
+        a_codes.data_ptr(), a_scales.data_ptr(), bt_codes.data_ptr(), bt_scales.data_ptr(), M, N, K,
+        out.data_ptr(), _stream(stream)))
+    return out
 
 
 def fp4_dequantize(fmt, codes, scales, alpha, rows, cols, flags=0, out=None, stream=None):

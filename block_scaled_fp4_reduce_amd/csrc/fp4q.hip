@@ -4,6 +4,7 @@
 
 #include "../../include/fp4q.h"
 #include "msed_kernels.h"
+#include "mxgemm_kernels.h"
 #include "mx_kernels.h"
 #include "nvfp4_2d_kernels.h"
 #include "nvfp4_kernels.h"
@@ -353,6 +354,33 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   launch_mxfp4(x, rows, cols, (flags & FP4_HAD32) != 0, rw ? codes_r : nullptr,
                rw ? scales_r : nullptr, cw ? codes_c : nullptr, cw ? scales_c : nullptr,
                (hipStream_t)stream, num_cus());
+  return launched();
+}
+
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* bt_codes,
+               const uint8_t* bt_scales, int64_t M, int64_t N, int64_t K, float* c,
+               void* stream) {
+  if (M < 0 || N < 0 || K < 0) return FP4_E_SHAPE;
+  if (K % kGemmBK) return FP4_E_SHAPE;
+  if ((M > 0 && K > 0 && (!a_codes || !a_scales)) || (N > 0 && K > 0 && (!bt_codes || !bt_scales)) ||
+      (M > 0 && N > 0 && !c))
+    return FP4_E_NULL;
+  // buffer resources span at most one tile of rows: keep them below 2 GiB
+  if (K >= ((int64_t)1 << 24) || N >= ((int64_t)1 << 21) || M >= ((int64_t)1 << 40) / (N > 0 ? N : 1))
+    return FP4_E_SHAPE;
+  if (!aligned(a_codes, 16) || !aligned(bt_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(bt_scales, 4) || !aligned(c, 4))
+    return FP4_E_ALIGN;
+  if (M == 0 || N == 0) return FP4_OK;
+  if (K == 0) {                           // empty sum: C = 0
+    int64_t grid = cdiv(M * N, 256);
+    if (grid > 4096) grid = 4096;
+    fill_zero_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(c, M * N);
+    return launched();
+  }
+  const int64_t tiles_n = cdiv(N, kGemmBN), tiles = cdiv(M, kGemmBM) * tiles_n;
+  mxfp4_gemm_kernel<<<(unsigned)tiles, kGemmThreads, 0, (hipStream_t)stream>>>(
+      a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, tiles_n);
   return launched();
 }
 

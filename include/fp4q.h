@@ -198,6 +198,25 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                    uint32_t flags, uint8_t* codes_r, uint8_t* scales_r,
                    uint8_t* codes_c, uint8_t* scales_c, void* stream);
 
+/* MXFP4 matrix product C = A B, the consumer of the quantized tensors
+ * (NVIDIA NVFP4 article sec. 1 and 5: MXFP4, E2M1 values with a UE8M0
+ * scale per 32, multiplied directly by block-scaled matrix hardware; AMD
+ * MI355X MXFP4 article sec. 2: training with both operands in MXFP4), on
+ * gfx950's block-scaled FP4 matrix instructions with fp32 accumulation.
+ *   a_codes [M][K/2], a_scales [M][K/32]   A in the row-wise MXFP4 layout
+ *                                          (mxfp4_quantize ROWWISE of A)
+ *   bt_codes [N][K/2], bt_scales [N][K/32] B^T in the same layout (the
+ *                                          COLWISE output of mxfp4_quantize
+ *                                          applied to B [K][N])
+ *   c  [M][N] fp32, row-major.
+ *   With HAD32 on both operands the rotations along K cancel in the product
+ *   (the 32-point Hadamard is orthonormal), up to rounding.
+ *   Shapes: K % 128 == 0; M, N >= 0.  Code buffers 16-byte aligned, scale
+ *   buffers and c 4-byte aligned. */
+int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* bt_codes,
+               const uint8_t* bt_scales, int64_t M, int64_t N, int64_t K, float* c,
+               void* stream);
+
 /* Dequantize to fp32 [rows][cols] (the decode applied by the consumer:
  * NVIDIA NVFP4 article sec. 4 and sec. 6).
  *   format FP4_FORMAT_NVFP4: out = q * (alpha * Delta), alpha = *alpha

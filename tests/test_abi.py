@@ -133,6 +133,19 @@ def test_rows_rejects(L):
     assert L.nvfp4_quantize_rows(None, 0, 64, 0, 0, None, None, None, None, None) == OK
 
 
+def test_gemm_rejects(L):
+    def gm(a=P, sa=F4, b=P, sb=F4, M=128, N=128, K=256, c=F4):
+        return L.mxfp4_gemm(a, sa, b, sb, M, N, K, c, None)
+    assert gm(a=None) == E_NULL
+    assert gm(sb=None) == E_NULL
+    assert gm(c=None) == E_NULL
+    assert gm(K=192) == E_SHAPE                  # K % 128
+    assert gm(M=-1) == E_SHAPE
+    assert gm(a=Q) == E_ALIGN
+    assert gm(sa=F4 + 1) == E_ALIGN
+    assert gm(M=0, a=None, sa=None, c=None) == OK  # empty product
+
+
 def test_mx_rejects(L):
     f = fp4.HAD32 | fp4.ROWWISE | fp4.COLWISE
     assert L.mxfp4_quantize(None, 64, 64, f, P, P, P, P, None) == E_NULL
