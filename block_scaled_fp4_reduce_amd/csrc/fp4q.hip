@@ -365,8 +365,9 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
   if ((M > 0 && K > 0 && (!a_codes || !a_scales)) || (N > 0 && K > 0 && (!bt_codes || !bt_scales)) ||
       (M > 0 && N > 0 && !c))
     return FP4_E_NULL;
-  // buffer resources span at most one tile of rows: keep them below 2 GiB
-  if (K >= ((int64_t)1 << 24) || N >= ((int64_t)1 << 21) || M >= ((int64_t)1 << 40) / (N > 0 ? N : 1))
+  // buffer resources and offsets span one 256-row tile: K < 2^23 and
+  // N < 2^20 keep them below 2^30 bytes
+  if (K >= ((int64_t)1 << 23) || N >= ((int64_t)1 << 20) || M >= ((int64_t)1 << 40) / (N > 0 ? N : 1))
     return FP4_E_SHAPE;
   if (!aligned(a_codes, 16) || !aligned(bt_codes, 16) || !aligned(a_scales, 4) ||
       !aligned(bt_scales, 4) || !aligned(c, 4))
@@ -378,9 +379,10 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
     fill_zero_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(c, M * N);
     return launched();
   }
-  const int64_t tiles_n = cdiv(N, kGemmBN), tiles = cdiv(M, kGemmBM) * tiles_n;
-  mxfp4_gemm_kernel<<<(unsigned)tiles, kGemmThreads, 0, (hipStream_t)stream>>>(
-      a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, tiles_n);
+  const int64_t tiles_m = cdiv(M, kGemmBM), tiles_n = cdiv(N, kGemmBN);
+  const int64_t slots = xcd_grid(tiles_m, tiles_n, kGemmSuperY, kGemmSuperX);
+  mxfp4_gemm_kernel<<<(unsigned)slots, kGemmThreads, 0, (hipStream_t)stream>>>(
+      a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, (uint32_t)tiles_m, (uint32_t)tiles_n);
   return launched();
 }
 

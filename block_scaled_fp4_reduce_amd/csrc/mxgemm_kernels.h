@@ -14,33 +14,39 @@
 // nibble) and its scale register the UE8M0 byte of those 32 values.  The
 // 16 accumulators of lane l are D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
 //
-// Workgroup: 256 threads, a 128 x 128 tile of C, each wave 64 x 64 (2 x 2
+// Workgroup: 512 threads, a 256 x 256 tile of C, each wave 128 x 64 (4 x 2
+// instructions per 64 values of K, six 16-byte operand reads for eight
 // instructions); K in steps of 128 values, staged in LDS (double buffered,
-// rows padded to 80 bytes so the 16-byte operand reads of eight
+// rows padded to 80 bytes so the 16-byte operand reads of 8 or 16
 // consecutive rows hit distinct banks), the next step's global loads in
-// flight during the current step's matrix work.  Rows past M or N read as
-// zeros through the buffer-resource bounds; stores past them are dropped.
+// flight during the current step's matrix work.  Tiles go out in XCD
+// super-tile order (4 x 8 tiles per XCD per round), so the workgroups that
+// share A and B K-slabs run on one L2 at the same time.  Rows past M or N
+// read as zeros through the buffer-resource bounds; stores past them are
+// dropped.
 #pragma once
 
 #include "device_common.h"
 
 namespace fp4q {
 
-constexpr int kGemmThreads = 256;
-constexpr int kGemmBM = 128, kGemmBN = 128;
+constexpr int kGemmThreads = 512;                  // 8 waves: 2 (M) x 4 (N)
+constexpr int kGemmBM = 256, kGemmBN = 256;        // C tile per workgroup
+constexpr int kGemmMI = 4, kGemmNJ = 2;            // 32 x 32 blocks per wave (128 x 64)
 constexpr int kGemmBK = 128;                       // K values per step
 constexpr int kGemmRowBytes = kGemmBK / 2;         // 64 code bytes per row per step
 constexpr int kGemmPitch = kGemmRowBytes + 16;     // LDS row pitch (bytes)
+constexpr int kGemmSuperY = 4, kGemmSuperX = 8;    // tiles per XCD super-tile
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // One K step of both operands, in registers between its global load and its
-// LDS store: two 16-byte pieces of each 8 KB tile per thread, and (threads
-// below 128) one row's four scale bytes of each.
+// LDS store: two 16-byte pieces of each 16 KB tile per thread, and one scale
+// dword (four K blocks of one row): A's for threads below 256, B's above.
 struct GemmStage {
   u32x4_t a0, a1, b0, b1;
-  uint32_t sa, sb;
+  uint32_t s;
 };
 
 __device__ __forceinline__ void gemm_load(GemmStage& g, __amdgpu_buffer_rsrc_t ra,
@@ -48,7 +54,7 @@ __device__ __forceinline__ void gemm_load(GemmStage& g, __amdgpu_buffer_rsrc_t r
                                           __amdgpu_buffer_rsrc_t rsb, int64_t K, int ks) {
   const int t = threadIdx.x;
   const int kb = ks * kGemmRowBytes;               // byte offset of the step in a code row
-  // piece q = t + 256 i: row q / 4, 16-byte column q % 4
+  // piece q = t + 512 i: row q / 4, 16-byte column q % 4
   const int r0 = t >> 2, r1 = (t + kGemmThreads) >> 2, c = 16 * (t & 3);
   const int rowb = (int)(K / 2);
   g.a0 = __builtin_bit_cast(u32x4_t, buffer_load16(ra, r0 * rowb + kb + c));
@@ -56,9 +62,8 @@ __device__ __forceinline__ void gemm_load(GemmStage& g, __amdgpu_buffer_rsrc_t r
   g.b0 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r0 * rowb + kb + c));
   g.b1 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r1 * rowb + kb + c));
   const int srow = (int)(K / 32), sb = ks * (kGemmBK / 32);
-  const int tr = t & 127;                          // threads >= 128 repeat rows (unused)
-  g.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, tr * srow + sb, 0, 0);
-  g.sb = __builtin_amdgcn_raw_buffer_load_b32(rsb, tr * srow + sb, 0, 0);
+  g.s = t < 256 ? __builtin_amdgcn_raw_buffer_load_b32(rsa, t * srow + sb, 0, 0)
+                : __builtin_amdgcn_raw_buffer_load_b32(rsb, (t - 256) * srow + sb, 0, 0);
 }
 
 __device__ __forceinline__ void gemm_store(const GemmStage& g, uint8_t* la, uint8_t* lb,
@@ -69,22 +74,21 @@ __device__ __forceinline__ void gemm_store(const GemmStage& g, uint8_t* la, uint
   *(u32x4_t*)(la + r1 * kGemmPitch + c) = g.a1;
   *(u32x4_t*)(lb + r0 * kGemmPitch + c) = g.b0;
   *(u32x4_t*)(lb + r1 * kGemmPitch + c) = g.b1;
-  if (t < 128) {
-    lsa[t] = g.sa;
-    lsb[t] = g.sb;
-  }
+  if (t < 256) lsa[t] = g.s;
+  else lsb[t - 256] = g.s;
 }
 
 __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ bt_codes, const uint8_t* __restrict__ bt_scales, int64_t M,
-    int64_t N, int64_t K, float* __restrict__ c_out, int64_t tiles_n) {
+    int64_t N, int64_t K, float* __restrict__ c_out, uint32_t tiles_m, uint32_t tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t lA[2][kGemmBM * kGemmPitch];
   __shared__ __attribute__((aligned(16))) uint8_t lB[2][kGemmBN * kGemmPitch];
   __shared__ uint32_t lsA[2][kGemmBM], lsB[2][kGemmBN];
 
-  const int64_t tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const int64_t m0 = tm * kGemmBM, n0 = tn * kGemmBN;
+  TileOrder to;
+  if (!xcd_tile<kGemmSuperY, kGemmSuperX>(blockIdx.x, tiles_m, tiles_n, to)) return;  // uniform
+  const int64_t m0 = to.ty * kGemmBM, n0 = to.tx * kGemmBN;
   const int64_t mrows = M - m0 < kGemmBM ? M - m0 : kGemmBM;
   const int64_t nrows = N - n0 < kGemmBN ? N - n0 : kGemmBN;
   // resources over this tile's rows of each operand (rows past M / N read 0)
@@ -98,13 +102,13 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
       const_cast<uint8_t*>(bt_scales + n0 * (K / 32)), 0, (int)(nrows * (K / 32)), 0x00020000);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 31, g = lane >> 5;
-  f32x16_t acc[2][2];
+  f32x16_t acc[kGemmMI][kGemmNJ];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < kGemmMI; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < kGemmNJ; j++) acc[i][j] = f32x16_t{};
 
   const int nk = (int)(K / kGemmBK);
   GemmStage st;
@@ -116,26 +120,26 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     if (ks + 1 < nk) gemm_load(st, ra, rb, rsa, rsb, K, ks + 1);
 #pragma unroll
     for (int s = 0; s < 2; s++) {                 // two 64-value halves of the step
-      i32x8_t av[2], bv[2];
-      int sa[2], sb[2];
+      i32x8_t av[kGemmMI], bv[kGemmNJ];
+      int sa[kGemmMI], sb[kGemmNJ];
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const int row = 64 * wm + 32 * i + r;
+      for (int i = 0; i < kGemmMI; i++) {
+        const int row = 128 * wm + 32 * i + r;
         const u32x4_t v = *(const u32x4_t*)(lA[cur] + row * kGemmPitch + 32 * s + 16 * g);
         av[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sa[i] = (int)((lsA[cur][row] >> (8 * (2 * s + g))) & 0xFFu);
       }
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
+      for (int j = 0; j < kGemmNJ; j++) {
         const int row = 64 * wn + 32 * j + r;
         const u32x4_t v = *(const u32x4_t*)(lB[cur] + row * kGemmPitch + 32 * s + 16 * g);
         bv[j] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sb[j] = (int)((lsB[cur][row] >> (8 * (2 * s + g))) & 0xFFu);
       }
 #pragma unroll
-      for (int i = 0; i < 2; i++)
+      for (int i = 0; i < kGemmMI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < kGemmNJ; j++)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               av[i], bv[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
     }
@@ -147,14 +151,14 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       c_out + m0 * N, 0, (int)(mrows * N * 4), 0x00020000);
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
+  for (int j = 0; j < kGemmNJ; j++) {
     const int64_t col = 64 * wn + 32 * j + r;
     if (col < nrows) {
 #pragma unroll
-      for (int i = 0; i < 2; i++)
+      for (int i = 0; i < kGemmMI; i++)
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-          const int64_t row = 64 * wm + 32 * i + 8 * (v / 4) + 4 * g + (v % 4);
+          const int64_t row = 128 * wm + 32 * i + 8 * (v / 4) + 4 * g + (v % 4);
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][v]), rc,
                                                 (int)((row * N + n0 + col) * 4), 0, 0);
         }

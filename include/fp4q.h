@@ -211,8 +211,8 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
  *   c  [M][N] fp32, row-major.
  *   With HAD32 on both operands the rotations along K cancel in the product
  *   (the 32-point Hadamard is orthonormal), up to rounding.
- *   Shapes: K % 128 == 0; M, N >= 0.  Code buffers 16-byte aligned, scale
- *   buffers and c 4-byte aligned. */
+ *   Shapes: K % 128 == 0, K < 2^23, N < 2^20, M*N < 2^40; M, N >= 0.  Code
+ *   buffers 16-byte aligned, scale buffers and c 4-byte aligned. */
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* bt_codes,
                const uint8_t* bt_scales, int64_t M, int64_t N, int64_t K, float* c,
                void* stream);
