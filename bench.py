@@ -336,9 +336,11 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0, w_np=None):
         elif kind == "requant":
             oracle.nvfp4_requantize_t(q["codes"], q["scales"], q["alpha"], x.shape[0], cols, flags,
                                       seed=SEED)
-        elif kind == "gemm":
-            oracle.mxfp4_gemm(qa["codes_r"], qa["scales_r"], qb["codes_r"], qb["scales_r"],
-                              x.shape[0], GEMM_N, cols)
+        elif kind == "gemm":                                 # BLAS held to one thread
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                oracle.mxfp4_gemm(qa["codes_r"], qa["scales_r"], qb["codes_r"], qb["scales_r"],
+                                  x.shape[0], GEMM_N, cols)
         else:
             oracle.mxfp4_quantize(x, flags)
         times.append(time.perf_counter() - t0)
