@@ -159,6 +159,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
+// Cache policy of quantizer output stores: non-temporal (streaming).  Codes
+// and scales are written once and never read back by the kernel, so they
+// should not displace input lines, and fewer dirty lines are left in L2
+// when the kernel ends.
+constexpr int kStoreNT = 2;
+
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
   const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);

@@ -154,6 +154,17 @@ __device__ __forceinline__ void build_scale_table(float2* tab, float alpha) {
   }
 }
 
+// The same table over all 256 byte values, for lookups by the raw byte the
+// FP8 conversion writes: bytes with the sign bit set (from NaN input only)
+// read the entry of their low seven bits.  Needs 256 threads.
+__device__ __forceinline__ void build_scale_table256(float2* tab, float alpha) {
+  static_assert(kThreads == 256, "one table entry per thread");
+  const uint32_t low = threadIdx.x & 0x7Fu;
+  const uint32_t code = low < 127 ? low : 126u;
+  const float s = alpha * e4m3_value(code);
+  tab[threadIdx.x] = make_float2(s, s == 0.0f ? 0.0f : 1.0f / s);
+}
+
 // Error of one dequantized pair against its inputs, accumulated with fma.
 template <int BYTE>
 __device__ __forceinline__ float err_pair(uint32_t packed, float s, float y0, float y1, float acc) {
@@ -243,6 +254,16 @@ __device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t& ca, uint32
   ca = e4m3_rne(a);
   cb = e4m3_rne(b);
 #endif
+}
+
+// Both E4M3 codes in one word: byte 0 is the code of a, byte 1 that of b
+// (after the same clamp to [0, 448] as e4m3_pair; the upper half is
+// arbitrary).  `any` is any live value: the conversion keeps the upper half
+// of its destination, so no register needs clearing first.
+__device__ __forceinline__ uint32_t e4m3_pair_word(float a, float b, uint32_t any) {
+  const float a2 = __builtin_amdgcn_fmed3f(a, 0.0f, 448.0f);
+  const float b2 = __builtin_amdgcn_fmed3f(b, 0.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, b2, (int)any, false);
 }
 
 // One quantized 16-value block: its two code words, E4M3 scale code and
@@ -337,34 +358,37 @@ __device__ __forceinline__ void nvfp4_block(uint4 v0, uint4 v1, int64_t b, const
 #pragma unroll
   for (int k = 0; k < 16; k++) amax_b = fmaxf(amax_b, fabsf(y[k]));
 
-  uint32_t e6, e4;
-  e4m3_pair(amax_b * k6, amax_b * k4, e6, e4);
-  const float2 sr6 = tab[e6];
+  // scale bytes straight from the conversion word: byte 0 (M = 6) and
+  // byte 1 (M = 4) index the 256-entry table as byte offsets
+  const uint32_t ew = e4m3_pair_word(amax_b * k6, amax_b * k4, v1.w);
+  const char* tb = (const char*)tab;
+  const float2 sr6 = *(const float2*)(tb + ((ew & 0xFFu) << 3));
   // every byte of the code words is written by the conversions, so they
-  // start from an arbitrary value (no zeroing instruction)
-  uint32_t w0 = __builtin_nondeterministic_value(0u), w1 = __builtin_nondeterministic_value(0u);
-  uint32_t scale = e6, pick4 = 0;
+  // start from whatever the input registers hold (no clearing instruction)
+  uint32_t w0 = v0.x, w1 = v0.y;
+  uint32_t scale = ew, pick4 = 0;             // the store keeps the low byte
   if constexpr (SR) {
     quant16_sr(y, sr6.x, sr6.y, (uint64_t)b * 16, seed_lo, seed_hi, w0, w1);
   } else {
     const float err6 = quant16_rtn(y, sr6.x, sr6.y, w0, w1);
     if constexpr (FOUR_SIX) {
-      const float2 sr4 = tab[e4];
-      uint32_t u0 = __builtin_nondeterministic_value(0u), u1 = __builtin_nondeterministic_value(0u);
+      const float2 sr4 = *(const float2*)(tb + (((ew >> 8) & 0xFFu) << 3));
+      uint32_t u0 = v0.z, u1 = v0.w;
       const float err4 = quant16_rtn(y, sr4.x, sr4.y, u0, u1);
       pick4 = err4 < err6 ? 1u : 0u;      // ties keep M = 6
       w0 = pick4 ? u0 : w0;
       w1 = pick4 ? u1 : w1;
-      scale = pick4 ? e4 : e6;
+      scale = pick4 ? ew >> 8 : ew;
     }
   }
   const int lane = threadIdx.x;
   i32x2_t cw;
   cw.x = (int)w0;
   cw.y = (int)w1;
-  __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * lane, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)scale, rs, lane, 0, 0);
-  if (want_choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)pick4, rh, lane, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * lane, 0, kStoreNT);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)scale, rs, lane, 0, kStoreNT);
+  if (want_choice)
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)pick4, rh, lane, 0, kStoreNT);
 }
 
 // 1D NVFP4: one lane per 16-value block of the flattened tensor (blocks never
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
     int namax, float* __restrict__ alpha_out, uint2* __restrict__ codes,
     uint8_t* __restrict__ scales, uint8_t* __restrict__ choice, uint32_t seed_lo,
     uint32_t seed_hi) {
-  __shared__ float2 tab[128];
+  __shared__ float2 tab[256];
   __shared__ float kshared[2];
   __shared__ uint32_t red[kThreads / 64];
   // chunk indices fit in 32 bits (rows*cols < 2^40 -> < 2^28 chunks), which
@@ -422,9 +446,9 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
     }
   }
   m = block_max_u32(m, red);
-  if (lane < 128) {                        // waves 0 and 1: tensor scale and table
+  {                                        // every lane: one table entry
     const TensorScale ts = tensor_scale(__uint_as_float(m), FOUR_SIX);
-    build_scale_table(tab, ts.alpha);
+    build_scale_table256(tab, ts.alpha);
     if (lane == 0) {
       kshared[0] = ts.k6;
       kshared[1] = ts.k4;
