@@ -92,9 +92,9 @@ __device__ __forceinline__ void msed_block(uint4 v0, uint4 v1, int64_t b, float 
   i32x2_t cw;
   cw.x = (int)w0;
   cw.y = (int)w1;
-  __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * lane, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)scale, rs, lane, 0, 0);
-  if (want_choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)0, rh, lane, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * lane, 0, kStoreNT);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)scale, rs, lane, 0, kStoreNT);
+  if (want_choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)0, rh, lane, 0, kStoreNT);
 }
 
 // The per-tensor quantizer's loop with the MS-EDEN block (see

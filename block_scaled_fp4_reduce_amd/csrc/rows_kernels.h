@@ -133,9 +133,9 @@ __device__ __forceinline__ void row_chunk_quant(const RowRegs<NB>& R, int64_t ro
       i32x2_t cw;
       cw.x = (int)o.w0;
       cw.y = (int)o.w1;
-      __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * j, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.scale, rs, j, 0, 0);
-      if (choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.pick4, rh, j, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * j, 0, kStoreNT);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.scale, rs, j, 0, kStoreNT);
+      if (choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.pick4, rh, j, 0, kStoreNT);
     }
   });
 }
@@ -319,9 +319,9 @@ __device__ __forceinline__ void wgrow_chunk_quant(const RowRegs<NB>& R, const Ro
       i32x2_t cw;
       cw.x = (int)o.w0;
       cw.y = (int)o.w1;
-      __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * j, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.scale, rs, j, 0, 0);
-      if (choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.pick4, rh, j, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(cw, rc, 8 * j, 0, kStoreNT);
+      __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.scale, rs, j, 0, kStoreNT);
+      if (choice) __builtin_amdgcn_raw_buffer_store_b8((unsigned char)o.pick4, rh, j, 0, kStoreNT);
     }
   });
 }
