@@ -14,11 +14,15 @@
 // whose result is bit-identical in every lane.  The transposed codes are
 // recomputed from an LDS copy of the tile with the same scale, so they are
 // the same fp32 operations on the same values and equal the row-wise codes
-// by construction.  Workgroups are persistent (the next 64x256 tile is
-// loaded while the current one is computed) and take tiles in XCD-aware
-// order (16x4 tiles per XCD super-tile, grid a multiple of 8) so the
-// transposed codes and the scale bytes that neighbouring tiles write into
-// one 64-byte segment are completed in the same L2.
+// by construction.  The codes of a workgroup tile (64 x 256 values) are
+// staged in LDS and leave in 16-byte runs: 128 bytes per row row-wise, 32
+// bytes per row of the transposed codes (a store that scatters 8-byte
+// pieces over 64 lines costs far more).  Workgroups are persistent (the
+// next tile is loaded while the current one is computed; three per CU, so
+// the per-tile barrier of one is covered by the others) and take tiles in
+// XCD-aware order (16x4 tiles per XCD super-tile, grid a multiple of 8) so
+// the transposed codes and the scale bytes that neighbouring tiles write
+// into one 64-byte segment are completed in the same L2.
 #pragma once
 
 #include "device_common.h"
@@ -30,10 +34,15 @@ constexpr bool kHave2D = true;
 constexpr int k2dStrips = 4;                 // 64-column strips per workgroup
 constexpr int k2dSuperY = 16, k2dSuperX = 4; // workgroups per XCD super-tile (1024x1024 values)
 constexpr int k2dTileLds = 16 * 16 + 16;     // bf16 per tile in LDS (+32 B pad: no bank conflicts)
+// Code staging per workgroup tile (64 rows x 256 columns), two buffers:
+// row-wise codes 64 rows x 128 B, transposed codes 256 rows x 32 B (pitches
+// padded against bank conflicts).
+constexpr int k2dRowPitch = 128 + 8;
+constexpr int k2dColPitch = 32 + 8;
 #ifndef FP4Q_2D_WG_PER_CU
-#define FP4Q_2D_WG_PER_CU 2
+#define FP4Q_2D_WG_PER_CU 3
 #endif
-constexpr int k2dWgPerCu = FP4Q_2D_WG_PER_CU; // persistent workgroups per CU
+constexpr int k2dWgPerCu = FP4Q_2D_WG_PER_CU; // persistent workgroups per CU (LDS 48 KiB each)
 
 struct Strips {   // one lane's tile row in each of the k2dStrips strips
   uint4 v[2 * k2dStrips];
@@ -60,6 +69,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   __shared__ float2 tab[128];
   __shared__ uint32_t red[kThreads / 64];
   __shared__ uint16_t stage[kThreads / 64][4][k2dTileLds];
+  __shared__ __align__(16) uint8_t cst_r[2][64 * k2dRowPitch];
+  __shared__ __align__(16) uint8_t cst_t[2][TRANSPOSE ? 256 * k2dColPitch : 8];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tile = lane >> 4, r = lane & 15;                 // tile in wave, row in tile
@@ -102,11 +113,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   };
 
   // Tile work; `to.ty < 0` (a slot with no tile) is uniform over the workgroup.
-  auto process = [&](const Strips& cur, const TileOrder& to) {
+  auto process = [&](const Strips& cur, const TileOrder& to, int buf) {
     if (to.ty < 0) return;
+    uint8_t* cs_row = cst_r[buf];
+    uint8_t* cs_col = cst_t[buf];
     const int64_t br = to.ty * 4 + wave;                 // tile row of this wave
     const bool row_ok = br < brows;
-    const int64_t row = br * 16 + r;
 #pragma unroll
     for (int s = 0; s < k2dStrips; s++) {
       const int64_t bc = (to.tx * k2dStrips + s) * 4 + tile;   // tile column
@@ -133,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
           w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
         }
       }
+      *(uint2*)(cs_row + (wave * 16 + r) * k2dRowPitch + (s * 4 + tile) * 8) = make_uint2(w0, w1);
       if (ok) {
-        *(uint2*)(codes + row * (cols / 2) + bc * 8) = make_uint2(w0, w1);
         if (r == 0) {
           scales[br * bcols + bc] = (uint8_t)scale;
           if (choice) choice[br * bcols + bc] = (uint8_t)pick4;
@@ -159,13 +171,65 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
         t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
         t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
         t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
-        if (ok) {
-          // column 16*tile + r, tile row br: 8 bytes; the 4 waves and the
-          // workgroup below (same XCD) complete the column's 64-byte segment
-          *(uint2*)(codes_t + (bc * 16 + r) * (rows / 2) + br * 8) = make_uint2(t0, t1);
-          if (r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
-        }
+        // column 16*tile + r of the strip, tile row `wave`: 8 bytes
+        *(uint2*)(cs_col + ((s * 4 + tile) * 16 + r) * k2dColPitch + wave * 8) = make_uint2(t0, t1);
+        if (ok && r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
         wave_lds_sync();                   // reads done before the next strip's writes
+      }
+    }
+    // Every wave's codes of this workgroup tile are staged: write them out
+    // in contiguous runs of 16 bytes (two tiles' codes in one row).
+    // Row-wise, 8 lanes cover one row's 128 bytes (a wave 8 rows);
+    // transposed, 2 lanes cover the 32 bytes this tile adds to one row of
+    // the transposed codes (a wave 32 rows).  At the tensor's edge a run may
+    // hold one valid tile: then only its 8 bytes are stored.  The other
+    // buffer takes the next tile, so one barrier per tile suffices.
+    __syncthreads();
+    const int64_t r0 = (int64_t)to.ty * 64, c0 = (int64_t)to.tx * 256;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const int k = (int)threadIdx.x + kThreads * i;
+      const int rr = k >> 3, j = k & 7;                  // 16 bytes: tiles 2j, 2j+1
+      const int64_t t0 = (int64_t)to.tx * 16 + 2 * j;
+      const uint8_t* src = cs_row + rr * k2dRowPitch + j * 16;
+      uint8_t* dst = codes + (r0 + rr) * (cols / 2) + (c0 >> 1) + j * 16;
+      if (r0 + rr < rows && t0 < bcols) {
+        const uint2 lo = *(const uint2*)src;
+        if (t0 + 1 < bcols) {
+          const uint2 hi = *(const uint2*)(src + 8);
+          if (((uintptr_t)dst & 15) == 0) {
+            *(uint4*)dst = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {                         // rows of cols/2 bytes: 8-byte aligned only
+            *(uint2*)dst = lo;
+            *(uint2*)(dst + 8) = hi;
+          }
+        } else {
+          *(uint2*)dst = lo;
+        }
+      }
+    }
+    if constexpr (TRANSPOSE) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int k = (int)threadIdx.x + kThreads * i;
+        const int cc = k >> 1, j = k & 1;                // 16 bytes: tile rows 2j, 2j+1
+        const int64_t t0 = (int64_t)to.ty * 4 + 2 * j;
+        const uint8_t* src = cs_col + cc * k2dColPitch + j * 16;
+        uint8_t* dst = codes_t + (c0 + cc) * (rows / 2) + (r0 >> 1) + j * 16;
+        if (c0 + cc < cols && t0 < brows) {
+          const uint2 lo = *(const uint2*)src;
+          if (t0 + 1 < brows) {
+            const uint2 hi = *(const uint2*)(src + 8);
+            if (((uintptr_t)dst & 15) == 0) {
+              *(uint4*)dst = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+              *(uint2*)dst = lo;
+              *(uint2*)(dst + 8) = hi;
+            }
+          } else {
+            *(uint2*)dst = lo;
+          }
+        }
       }
     }
   };
@@ -179,11 +243,11 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   while (slot < nslots) {
     const uint32_t s1 = slot + gridDim.x;    // grid is a multiple of 8: same XCD
     load(s1, sb, ob);
-    process(sa, oa);
+    process(sa, oa, 0);
     if (s1 >= nslots) break;
     const uint32_t s2 = s1 + gridDim.x;
     load(s2, sa, oa);
-    process(sb, ob);
+    process(sb, ob, 1);
     slot = s2;
   }
 }
