@@ -6,14 +6,16 @@
 // (a fixed, deterministic Hadamard rotation before quantizing, for both
 // operands of the weight-gradient product, hence both orientations).
 //
-// Mapping onto the chip.  A workgroup of 8 waves owns a 256x256 region,
+// Mapping onto the chip.  A workgroup of 16 waves (one per CU, four per
+// SIMD; 8 waves run 6 % slower) owns a 256x256 region,
 // processed as four 128x128 tiles, each staged through LDS, so every global
 // access is a full, coalesced segment (the kernel is bound by the memory
 // pipeline, not by arithmetic, once the rotation runs on the matrix cores):
 //  1. a tile is read with 16-byte non-temporal loads, 16 lanes per
 //     256-byte row piece, and written to LDS (the next tile's loads are
 //     already in flight);
-//  2. each wave quantizes two 32x32 blocks row-wise and two column-wise,
+//  2. each wave quantizes one 32x32 block row-wise and one column-wise
+//     (two each with 8 waves),
 //     staging codes and scales of the whole region in LDS;
 //  3. after the region's fourth tile, every region row (and column) leaves
 //     as one full 128-byte code line (eight lanes of 16 bytes) and 8 scale
@@ -49,7 +51,7 @@ constexpr bool kHaveMx = true;
 #define FP4Q_MX_WG_PER_CU 1
 #endif
 #ifndef FP4Q_MX_WAVES
-#define FP4Q_MX_WAVES 8
+#define FP4Q_MX_WAVES 16
 #endif
 constexpr int kMxWaves = FP4Q_MX_WAVES;          // 8 or 16 waves per workgroup
 constexpr int kMxThreads = 64 * kMxWaves;
