@@ -163,9 +163,9 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 // kernels whose waves write whole contiguous runs of codes and scales.  The
 // outputs are written once and never read back by the kernel, so they should
 // not displace input lines, and fewer dirty lines are left in L2 when the
-// kernel ends.  Kernels whose 64-byte segments are completed piecewise by
-// several tiles (2D, MX, requantization) keep ordinary stores: streaming
-// partial lines there costs far more than it saves.
+// kernel ends.  Segments completed piecewise by several tiles (the 2D
+// kernel's transposed codes, MX, requantization) keep ordinary stores:
+// streaming partial lines there costs far more than it saves.
 constexpr int kStoreNT = 2;
 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {

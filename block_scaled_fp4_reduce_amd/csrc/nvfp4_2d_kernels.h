@@ -39,6 +39,7 @@ constexpr int k2dTileLds = 16 * 16 + 16;     // bf16 per tile in LDS (+32 B pad:
 // padded against bank conflicts).
 constexpr int k2dRowPitch = 128 + 8;
 constexpr int k2dColPitch = 32 + 8;
+typedef unsigned int u32x4_nt_t __attribute__((ext_vector_type(4)));
 #ifndef FP4Q_2D_WG_PER_CU
 #define FP4Q_2D_WG_PER_CU 3
 #endif
@@ -198,7 +199,13 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
         if (t0 + 1 < bcols) {
           const uint2 hi = *(const uint2*)(src + 8);
           if (((uintptr_t)dst & 15) == 0) {
-            *(uint4*)dst = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            // a row's 128 bytes leave whole from one wave: streaming store
+            u32x4_nt_t v;
+            v.x = lo.x;
+            v.y = lo.y;
+            v.z = hi.x;
+            v.w = hi.y;
+            __builtin_nontemporal_store(v, (u32x4_nt_t*)dst);
           } else {                         // rows of cols/2 bytes: 8-byte aligned only
             *(uint2*)dst = lo;
             *(uint2*)(dst + 8) = hi;
