@@ -416,8 +416,34 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   const int G = gridDim.x;
   const int lane = threadIdx.x;
   const bool want_choice = choice != nullptr;
-  auto nblk = [&](int cc) { return cc < nchunks - 1 ? kThreads : (cc == nchunks - 1 ? tail : 0); };
-  auto in_rsrc = [&](int cc) {
+  // blocks in chunk cc: none outside [0, nchunks) (signed compares: with an
+  // empty tensor nchunks - 1 is -1)
+  auto nblk = [&](int cc) {
+    return (cc >= 0 && cc < nchunks - 1) ? kThreads : (cc == nchunks - 1 && cc >= 0 ? tail : 0);
+  };
+  // Chunk order.  The amax pass leaves the last quarter or so of what each
+  // XCD read in that XCD's L2 (it takes 64 KiB chunks, chunk a on XCD a % 8
+  // when its grid is a multiple of 8, in rising order).  With a grid that is
+  // a multiple of 8, workgroups here take virtual chunk indices v = w + i G
+  // and map them so that XCD x gets exactly the 8 KiB chunks q with
+  // (q / 8) % 8 == x, highest first: k = (G/8) i + w/8 counts XCD x's chunks,
+  // q = 64 (top - k/8) + 8 x + k % 8.  The virtual range is padded to a
+  // multiple of 64; indices past the end map to chunks >= nchunks, which
+  // read and write nothing.  Not used with RHT16 (its amax pass walks the
+  // tensor in another order, and the kernel is ALU-bound).
+  const bool remap_on = !RHT && (G & 7) == 0;
+  const int top = (nchunks - 1) >> 6;                  // -1 for an empty tensor
+  const int nvirt = remap_on ? 64 * (top + 1) : nchunks;
+  // v = blockIdx.x + i G is this workgroup's i-th virtual chunk
+  const int k0 = (int)blockIdx.x >> 3, x0 = (int)blockIdx.x & 7, kstep = G >> 3;
+  auto chunk_of = [&](int v, int i) {
+    if (!remap_on) return v;
+    if (v >= nvirt) return nchunks;                     // prefetch past the end: nothing
+    const int k = kstep * i + k0;
+    return 64 * (top - (k >> 3)) + 8 * x0 + (k & 7);
+  };
+  auto in_rsrc = [&](int v, int i) {
+    const int cc = chunk_of(v, i);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(x + 2 * (int64_t)cc * kThreads), 0,
                                              nblk(cc) * 32, 0x00020000);
   };
@@ -428,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   int c = blockIdx.x;
   uint4 a0, a1, b0, b1;
   {                                        // in flight during the prologue
-    const __amdgpu_buffer_rsrc_t r = in_rsrc(c);
+    const __amdgpu_buffer_rsrc_t r = in_rsrc(c, 0);
     a0 = buffer_load16(r, 32 * lane);
     a1 = buffer_load16(r, 32 * lane + 16);
   }
@@ -460,7 +486,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   uint32_t signs = 0;
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
 
-  auto process = [&](int cc, uint4 v0, uint4 v1) {
+  auto process = [&](int v, int i, uint4 v0, uint4 v1) {
+    const int cc = chunk_of(v, i);
     const int n = nblk(cc);
     const int64_t b0 = (int64_t)cc * kThreads;
     nvfp4_block<FOUR_SIX, SR, RHT>(
@@ -472,23 +499,25 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
         want_choice);
   };
 
-  while (c < nchunks) {
+  int it = 0;                              // c = blockIdx.x + it G
+  while (c < nvirt) {
     const int cb = c + G;
     {
-      const __amdgpu_buffer_rsrc_t r = in_rsrc(cb);
+      const __amdgpu_buffer_rsrc_t r = in_rsrc(cb, it + 1);
       b0 = buffer_load16(r, 32 * lane);
       b1 = buffer_load16(r, 32 * lane + 16);
     }
-    process(c, a0, a1);
-    if (cb >= nchunks) break;
+    process(c, it, a0, a1);
+    if (cb >= nvirt) break;
     const int ca = cb + G;
     {
-      const __amdgpu_buffer_rsrc_t r = in_rsrc(ca);
+      const __amdgpu_buffer_rsrc_t r = in_rsrc(ca, it + 2);
       a0 = buffer_load16(r, 32 * lane);
       a1 = buffer_load16(r, 32 * lane + 16);
     }
-    process(cb, b0, b1);
+    process(cb, it + 1, b0, b1);
     c = ca;
+    it += 2;
   }
 }
 
