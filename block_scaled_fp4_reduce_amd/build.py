@@ -64,6 +64,6 @@ def dump_asm(out_dir: str) -> str:
 
 if __name__ == "__main__":
     if "--asm" in sys.argv:
-        print(dump_asm(os.path.join(os.path.dirname(HERE), "_work", "asm")))
+        print(dump_asm(os.path.join(os.path.dirname(HERE), "_build", "asm")))
     else:
         print(build(verbose=True))
