@@ -18,8 +18,8 @@
 // instructions per 64 values of K, six 16-byte operand reads for eight
 // instructions); K in steps of 128 values, staged in LDS (double buffered,
 // rows padded to 80 bytes so the 16-byte operand reads of 8 or 16
-// consecutive rows hit distinct banks), the next step's global loads in
-// flight during the current step's matrix work.  Tiles go out in XCD
+// consecutive rows hit distinct banks), global loads issued two steps
+// ahead (two register staging sets).  Tiles go out in XCD
 // super-tile order (4 x 8 tiles per XCD per round), so the workgroups that
 // share A and B K-slabs run on one L2 at the same time.  Rows past M or N
 // read as zeros through the buffer-resource bounds; stores past them are
@@ -62,8 +62,13 @@ __device__ __forceinline__ void gemm_load(GemmStage& g, __amdgpu_buffer_rsrc_t r
   g.b0 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r0 * rowb + kb + c));
   g.b1 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r1 * rowb + kb + c));
   const int srow = (int)(K / 32), sb = ks * (kGemmBK / 32);
-  g.s = t < 256 ? __builtin_amdgcn_raw_buffer_load_b32(rsa, t * srow + sb, 0, 0)
-                : __builtin_amdgcn_raw_buffer_load_b32(rsb, (t - 256) * srow + sb, 0, 0);
+  // waves 0-3 load A's scales, waves 4-7 B's: the choice is uniform over a
+  // wave, said so explicitly, so it is one load through a scalar-selected
+  // resource (a per-lane choice of resource would become a loop over its
+  // values and blur the compiler's count of loads in flight)
+  const int half = __builtin_amdgcn_readfirstlane(t >> 8);
+  const __amdgpu_buffer_rsrc_t rs = half ? rsb : rsa;
+  g.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (t - 256 * half) * srow + sb, 0, 0);
 }
 
 __device__ __forceinline__ void gemm_store(const GemmStage& g, uint8_t* la, uint8_t* lb,
@@ -111,13 +116,25 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     for (int j = 0; j < kGemmNJ; j++) acc[i][j] = f32x16_t{};
 
   const int nk = (int)(K / kGemmBK);
-  GemmStage st;
-  gemm_load(st, ra, rb, rsa, rsb, K, 0);
-  gemm_store(st, lA[0], lB[0], lsA[0], lsB[0]);
+  // Two register staging sets: step j's global loads are issued two steps
+  // ahead (during step j - 2) and stored to LDS at the end of step j - 1,
+  // so they have two steps of matrix work to arrive.  The loop is unrolled
+  // by two so that each set is named at compile time (a runtime index
+  // would put the sets in scratch memory).
+  // Loads for steps past the end are issued too (unconditional loads keep
+  // the compiler's count of loads in flight exact, so each wait is for the
+  // right step): buffer loads are bounds-checked against the operand rows,
+  // and those registers are never stored to LDS.
+  GemmStage st0, st1;
+  gemm_load(st0, ra, rb, rsa, rsb, K, 0);
+  gemm_load(st1, ra, rb, rsa, rsb, K, 1);
+  gemm_store(st0, lA[0], lB[0], lsA[0], lsB[0]);
   __syncthreads();
-  for (int ks = 0; ks < nk; ks++) {
-    const int cur = ks & 1;
-    if (ks + 1 < nk) gemm_load(st, ra, rb, rsa, rsb, K, ks + 1);
+  // one K step: prefetch step ks + 2 into `mine` (free: its data went to LDS
+  // last step), multiply from LDS buffer `b`, store step ks + 1 (in
+  // `other`) to the other buffer
+  auto step = [&](int ks, GemmStage& mine, GemmStage& other, int b) {
+    gemm_load(mine, ra, rb, rsa, rsb, K, ks + 2);
 #pragma unroll
     for (int s = 0; s < 2; s++) {                 // two 64-value halves of the step
       i32x8_t av[kGemmMI], bv[kGemmNJ];
@@ -125,16 +142,16 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < kGemmMI; i++) {
         const int row = 128 * wm + 32 * i + r;
-        const u32x4_t v = *(const u32x4_t*)(lA[cur] + row * kGemmPitch + 32 * s + 16 * g);
+        const u32x4_t v = *(const u32x4_t*)(lA[b] + row * kGemmPitch + 32 * s + 16 * g);
         av[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sa[i] = (int)((lsA[cur][row] >> (8 * (2 * s + g))) & 0xFFu);
+        sa[i] = (int)((lsA[b][row] >> (8 * (2 * s + g))) & 0xFFu);
       }
 #pragma unroll
       for (int j = 0; j < kGemmNJ; j++) {
         const int row = 64 * wn + 32 * j + r;
-        const u32x4_t v = *(const u32x4_t*)(lB[cur] + row * kGemmPitch + 32 * s + 16 * g);
+        const u32x4_t v = *(const u32x4_t*)(lB[b] + row * kGemmPitch + 32 * s + 16 * g);
         bv[j] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sb[j] = (int)((lsB[cur][row] >> (8 * (2 * s + g))) & 0xFFu);
+        sb[j] = (int)((lsB[b][row] >> (8 * (2 * s + g))) & 0xFFu);
       }
 #pragma unroll
       for (int i = 0; i < kGemmMI; i++)
@@ -143,8 +160,12 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
               av[i], bv[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
     }
-    if (ks + 1 < nk) gemm_store(st, lA[cur ^ 1], lB[cur ^ 1], lsA[cur ^ 1], lsB[cur ^ 1]);
+    if (ks + 1 < nk) gemm_store(other, lA[b ^ 1], lB[b ^ 1], lsA[b ^ 1], lsB[b ^ 1]);
     __syncthreads();
+  };
+  for (int ks = 0; ks < nk; ks += 2) {
+    step(ks, st0, st1, 0);
+    if (ks + 1 < nk) step(ks + 1, st1, st0, 1);
   }
 
   // C tile: lane holds D[8 (v / 4) + 4 g + v % 4][r] of each 32 x 32 block
