@@ -14,25 +14,26 @@
 // nibble) and its scale register the UE8M0 byte of those 32 values.  The
 // 16 accumulators of lane l are D[8 (i / 4) + 4 (l / 32) + i % 4][l % 32].
 //
-// Workgroup: 512 threads, a 256 x 256 tile of C, each wave 128 x 64 (4 x 2
-// instructions per 64 values of K, six 16-byte operand reads for eight
-// instructions); K in steps of 128 values, staged in LDS (double buffered,
-// rows padded to 80 bytes so the 16-byte operand reads of 8 or 16
-// consecutive rows hit distinct banks), global loads issued two steps
-// ahead (two register staging sets).  Tiles go out in XCD
-// super-tile order (4 x 8 tiles per XCD per round), so the workgroups that
-// share A and B K-slabs run on one L2 at the same time.  Rows past M or N
-// read as zeros through the buffer-resource bounds; stores past them are
-// dropped.
+// Workgroup: 256 threads, a 256 x 256 tile of C, each of the 4 waves (one per
+// SIMD) 128 x 128 (4 x 4 instructions per 64 values of K, eight 16-byte
+// operand reads for sixteen instructions: with 8 waves of 128 x 64 the LDS
+// operand reads were as long as the matrix work, and the kernel ran 5 %
+// slower); K in steps of 128 values, staged in LDS (double buffered, rows
+// padded to 80 bytes so the 16-byte operand reads of 8 or 16 consecutive
+// rows hit distinct banks), global loads issued two steps ahead (two
+// register staging sets).  Tiles go out in XCD super-tile order (4 x 8
+// tiles per XCD per round), so the workgroups that share A and B K-slabs
+// run on one L2 at the same time.  Rows past M or N read as zeros through
+// the buffer-resource bounds; stores past them are dropped.
 #pragma once
 
 #include "device_common.h"
 
 namespace fp4q {
 
-constexpr int kGemmThreads = 512;                  // 8 waves: 2 (M) x 4 (N)
+constexpr int kGemmThreads = 256;                  // 4 waves: 2 (M) x 2 (N)
 constexpr int kGemmBM = 256, kGemmBN = 256;        // C tile per workgroup
-constexpr int kGemmMI = 4, kGemmNJ = 2;            // 32 x 32 blocks per wave (128 x 64)
+constexpr int kGemmMI = 4, kGemmNJ = 4;            // 32 x 32 blocks per wave (128 x 128)
 constexpr int kGemmBK = 128;                       // K values per step
 constexpr int kGemmRowBytes = kGemmBK / 2;         // 64 code bytes per row per step
 constexpr int kGemmPitch = kGemmRowBytes + 16;     // LDS row pitch (bytes)
@@ -42,45 +43,42 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // One K step of both operands, in registers between its global load and its
-// LDS store: two 16-byte pieces of each 16 KB tile per thread, and one scale
-// dword (four K blocks of one row): A's for threads below 256, B's above.
+// LDS store: four 16-byte pieces of each 16 KB tile per thread (piece q =
+// t + 256 i: row q / 4, 16-byte column q % 4), and one scale dword (four K
+// blocks of row t) of each operand.
 struct GemmStage {
-  u32x4_t a0, a1, b0, b1;
-  uint32_t s;
+  u32x4_t a[4], b[4];
+  uint32_t sa, sb;
 };
 
 __device__ __forceinline__ void gemm_load(GemmStage& g, __amdgpu_buffer_rsrc_t ra,
                                           __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rsa,
                                           __amdgpu_buffer_rsrc_t rsb, int64_t K, int ks) {
   const int t = threadIdx.x;
-  const int kb = ks * kGemmRowBytes;               // byte offset of the step in a code row
-  // piece q = t + 512 i: row q / 4, 16-byte column q % 4
-  const int r0 = t >> 2, r1 = (t + kGemmThreads) >> 2, c = 16 * (t & 3);
+  const int kb = ks * kGemmRowBytes;
   const int rowb = (int)(K / 2);
-  g.a0 = __builtin_bit_cast(u32x4_t, buffer_load16(ra, r0 * rowb + kb + c));
-  g.a1 = __builtin_bit_cast(u32x4_t, buffer_load16(ra, r1 * rowb + kb + c));
-  g.b0 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r0 * rowb + kb + c));
-  g.b1 = __builtin_bit_cast(u32x4_t, buffer_load16(rb, r1 * rowb + kb + c));
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int q = t + kGemmThreads * i, row = q >> 2, c = 16 * (q & 3);
+    g.a[i] = __builtin_bit_cast(u32x4_t, buffer_load16(ra, row * rowb + kb + c));
+    g.b[i] = __builtin_bit_cast(u32x4_t, buffer_load16(rb, row * rowb + kb + c));
+  }
   const int srow = (int)(K / 32), sb = ks * (kGemmBK / 32);
-  // waves 0-3 load A's scales, waves 4-7 B's: the choice is uniform over a
-  // wave, said so explicitly, so it is one load through a scalar-selected
-  // resource (a per-lane choice of resource would become a loop over its
-  // values and blur the compiler's count of loads in flight)
-  const int half = __builtin_amdgcn_readfirstlane(t >> 8);
-  const __amdgpu_buffer_rsrc_t rs = half ? rsb : rsa;
-  g.s = __builtin_amdgcn_raw_buffer_load_b32(rs, (t - 256 * half) * srow + sb, 0, 0);
+  g.sa = __builtin_amdgcn_raw_buffer_load_b32(rsa, t * srow + sb, 0, 0);
+  g.sb = __builtin_amdgcn_raw_buffer_load_b32(rsb, t * srow + sb, 0, 0);
 }
 
 __device__ __forceinline__ void gemm_store(const GemmStage& g, uint8_t* la, uint8_t* lb,
                                            uint32_t* lsa, uint32_t* lsb) {
   const int t = threadIdx.x;
-  const int r0 = t >> 2, r1 = (t + kGemmThreads) >> 2, c = 16 * (t & 3);
-  *(u32x4_t*)(la + r0 * kGemmPitch + c) = g.a0;
-  *(u32x4_t*)(la + r1 * kGemmPitch + c) = g.a1;
-  *(u32x4_t*)(lb + r0 * kGemmPitch + c) = g.b0;
-  *(u32x4_t*)(lb + r1 * kGemmPitch + c) = g.b1;
-  if (t < 256) lsa[t] = g.s;
-  else lsb[t - 256] = g.s;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int q = t + kGemmThreads * i, row = q >> 2, c = 16 * (q & 3);
+    *(u32x4_t*)(la + row * kGemmPitch + c) = g.a[i];
+    *(u32x4_t*)(lb + row * kGemmPitch + c) = g.b[i];
+  }
+  lsa[t] = g.sa;
+  lsb[t] = g.sb;
 }
 
 __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
@@ -107,7 +105,7 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
       const_cast<uint8_t*>(bt_scales + n0 * (K / 32)), 0, (int)(nrows * (K / 32)), 0x00020000);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   f32x16_t acc[kGemmMI][kGemmNJ];
 #pragma unroll
@@ -148,7 +146,7 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
       }
 #pragma unroll
       for (int j = 0; j < kGemmNJ; j++) {
-        const int row = 64 * wn + 32 * j + r;
+        const int row = 128 * wn + 32 * j + r;
         const u32x4_t v = *(const u32x4_t*)(lB[b] + row * kGemmPitch + 32 * s + 16 * g);
         bv[j] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
         sb[j] = (int)((lsB[b][row] >> (8 * (2 * s + g))) & 0xFFu);
@@ -173,7 +171,7 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
       c_out + m0 * N, 0, (int)(mrows * N * 4), 0x00020000);
 #pragma unroll
   for (int j = 0; j < kGemmNJ; j++) {
-    const int64_t col = 64 * wn + 32 * j + r;
+    const int64_t col = 128 * wn + 32 * j + r;
     if (col < nrows) {
 #pragma unroll
       for (int i = 0; i < kGemmMI; i++)
