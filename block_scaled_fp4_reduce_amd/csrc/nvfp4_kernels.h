@@ -499,8 +499,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
         want_choice);
   };
 
+  // Two chunks per trip, the next one's loads in flight.  The first trip is
+  // peeled off the loop so that the loop is entered with the same loads and
+  // stores in flight as at its back edge: the compiler then waits only for
+  // the chunk about to be computed, not for the previous chunk's stores.
   int it = 0;                              // c = blockIdx.x + it G
-  while (c < nvirt) {
+  auto trip = [&]() -> bool {              // false: no chunk left after this trip
     const int cb = c + G;
     {
       const __amdgpu_buffer_rsrc_t r = in_rsrc(cb, it + 1);
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
       b1 = buffer_load16(r, 32 * lane + 16);
     }
     process(c, it, a0, a1);
-    if (cb >= nvirt) break;
+    if (cb >= nvirt) return false;
     const int ca = cb + G;
     {
       const __amdgpu_buffer_rsrc_t r = in_rsrc(ca, it + 2);
@@ -518,6 +522,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
     process(cb, it + 1, b0, b1);
     c = ca;
     it += 2;
+    return true;
+  };
+  if (c < nvirt && trip()) {
+    while (c < nvirt) {
+      if (!trip()) break;
+    }
   }
 }
 
