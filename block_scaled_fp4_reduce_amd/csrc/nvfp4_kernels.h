@@ -486,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   uint32_t signs = 0;
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
 
-  auto process = [&](int v, int i, uint4 v0, uint4 v1) {
+  auto process = [&](int v, int i, uint4 v0, uint4 v1) __attribute__((always_inline)) {
     const int cc = chunk_of(v, i);
     const int n = nblk(cc);
     const int64_t b0 = (int64_t)cc * kThreads;
@@ -504,7 +504,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   // stores in flight as at its back edge: the compiler then waits only for
   // the chunk about to be computed, not for the previous chunk's stores.
   int it = 0;                              // c = blockIdx.x + it G
-  auto trip = [&]() -> bool {              // false: no chunk left after this trip
+  // (forced inline: out of line, the registers it shares would live in scratch)
+  auto trip = [&]() __attribute__((always_inline)) -> bool {   // false: no chunk left after it
     const int cb = c + G;
     {
       const __amdgpu_buffer_rsrc_t r = in_rsrc(cb, it + 1);
