@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_msed_kernel(
   uint32_t signs = 0;
   if constexpr (RHT) signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
 
-  auto process = [&](int cc, uint4 v0, uint4 v1) {
+  auto process = [&](int cc, uint4 v0, uint4 v1) __attribute__((always_inline)) {
     const int n = nblk(cc);
     const int64_t bb = (int64_t)cc * kThreads;
     msed_block<RHT>(v0, v1, bb + lane, ts.alpha, ts.k6, signs, seed_lo, seed_hi,
@@ -146,7 +146,11 @@ __global__ __launch_bounds__(kThreads) void nvfp4_msed_kernel(
                     want_choice);
   };
 
-  while (c < nchunks) {
+  // Two chunks per trip, the next one's loads in flight; the first trip is
+  // peeled off the loop so that the loop is entered with the same loads and
+  // stores in flight as at its back edge, and each wait covers only the
+  // chunk about to be computed (as in the 1D quantizer).
+  auto trip = [&]() __attribute__((always_inline)) -> bool {
     const int cb = c + G;
     {
       const __amdgpu_buffer_rsrc_t r = in_rsrc(cb);
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_msed_kernel(
       b1 = buffer_load16(r, 32 * lane + 16);
     }
     process(c, a0, a1);
-    if (cb >= nchunks) break;
+    if (cb >= nchunks) return false;
     const int ca = cb + G;
     {
       const __amdgpu_buffer_rsrc_t r = in_rsrc(ca);
@@ -163,6 +167,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_msed_kernel(
     }
     process(cb, b0, b1);
     c = ca;
+    return true;
+  };
+  if (c < nchunks && trip()) {
+    while (c < nchunks) {
+      if (!trip()) break;
+    }
   }
 }
 
