@@ -81,7 +81,8 @@ void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int na
                float* alpha_out, uint8_t* codes, uint8_t* scales, uint8_t* choice,
                uint64_t seed, hipStream_t st) {
   int64_t grid = nblocks > 0 ? cdiv(nblocks, (int64_t)kThreads) : 1;
-  if (grid > (int64_t)num_cus() * kWgPerCu) grid = (int64_t)num_cus() * kWgPerCu;
+  const int64_t resident = (int64_t)num_cus() * (SR ? kWgPerCu : kWgPerCuNoSr);
+  if (grid > resident) grid = resident;
   nvfp4_1d_kernel<F46, SR, RHT><<<(unsigned)grid, kThreads, 0, st>>>(
       (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
       (uint32_t)seed, (uint32_t)(seed >> 32));

@@ -44,6 +44,14 @@ constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
 constexpr int kAmaxThreads = FP4Q_AMAX_THREADS;
 constexpr int kBpt = FP4Q_BPT;              // 16-value blocks per lane per chunk (1D quantizer)
 constexpr int kWgPerCu = FP4Q_WG_PER_CU;    // resident 1D-quantizer workgroups per CU
+// Without SR the 1D quantizer needs at most 64 VGPRs, so six 4-wave
+// workgroups fit per CU (six waves per SIMD), which covers its loads better
+// than four (8192x4096 4/6: quantize 17.3 -> 16.4 us); the SR variants need
+// about 100 VGPRs for Philox, so four waves per SIMD is all that fits.
+#ifndef FP4Q_WG_PER_CU_NOSR
+#define FP4Q_WG_PER_CU_NOSR 6
+#endif
+constexpr int kWgPerCuNoSr = FP4Q_WG_PER_CU_NOSR;
 
 template <bool RHT>
 __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
