@@ -31,7 +31,7 @@ namespace fp4q {
 constexpr int kRowThreads = 256;
 constexpr int kRowWaves = kRowThreads / 64;
 #ifndef FP4Q_ROW_WG_PER_CU
-#define FP4Q_ROW_WG_PER_CU 4
+#define FP4Q_ROW_WG_PER_CU 6
 #endif
 constexpr int kRowWgPerCu = FP4Q_ROW_WG_PER_CU;   // cap on resident workgroups per CU
 
