@@ -10,16 +10,27 @@ in the 256 MB last-level cache.  Every launch goes through the library's C
 entry points with preallocated buffers, so the GPU, not the host, sets the
 pace.
 
-Reported on one JSON line: effective GB/s over the algorithmic bytes (bf16
-read + FP4 codes + E4M3 scales + 4 B tensor scale), the fraction of the
-8 TB/s HBM peak, the quantize kernel alone (amax given) timed with HIP
-events on its stream, rocprofv3 traffic for that kernel (when the committed
-counter summary matches the current kernel sources), the same figures for
-the other four workloads and for the requantization of a quantized
-activation and gradient for the transposed operand under "rows", and the CPU
-oracle timed on the host.
+Reported on one JSON line:
+  * value / ms_per_step: effective GB/s of the whole step over the
+    algorithmic bytes (bf16 read + FP4 codes + E4M3 scales + 4 B tensor
+    scale), timed over exactly --steps steps with HIP events;
+  * the quantize kernel alone (amax given), over >= 100 launches: the mean
+    of back-to-back launches (events around the whole run) and the median,
+    p10 and p90 over batches of 10 back-to-back launches (per-launch
+    durations of single kernels are in the rocprofv3 kernel-trace summary);
+  * the roofline of that kernel: HBM (algorithmic bytes / mean launch time
+    against 8 TB/s) and vector-ALU issue (issue slots per launch from the
+    committed rocprofv3 counter summary, against 614.4 G wave64 issue slots
+    per second: 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles); `bound` names the
+    larger fraction.  Traffic (FETCH_SIZE + WRITE_SIZE, calibrated) and the
+    issue slots come from that summary only while the kernel sources it was
+    taken on are unchanged, else null;
+  * the same figures for the other workloads under "rows";
+  * the CPU oracle on the host, single-threaded and on all cores of the
+    host's share (rows split over worker processes, arithmetic unchanged),
+    with the core count and CPU model.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu] [--no-rows]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-rows]
     python bench.py --summarize OUT.md DIR [DIR...]   # rocprofv3 output -> summary
 """
 from __future__ import annotations
@@ -35,6 +46,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# wave64 VALU issue slots per second: 256 CUs x 4 SIMDs, one wave64
+# instruction per SIMD every 4 cycles at 2.4 GHz (= 78.6 TFLOP/s of
+# non-packed fp32 FMA; packed fp32 is not used)
+VALU_PEAK_GSLOTS = 256 * 4 * 2.4 / 4
+MFMA_FP4_PEAK_TFLOPS = 10100.0                  # dense FP4 matrix peak of MI355X
+MIN_LAUNCHES = 100                               # kernel-only figures: launches timed
 # the kernel that does each workload's quantization (amax given)
 KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c2": "nvfp4_1d_kernel<true, false, false>",
@@ -46,8 +63,20 @@ KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "f3": "mxfp4_gemm_kernel",
              "f4a": "rq_quant_kernel<true, false, true>",
              "f4g": "rq_quant_kernel<false, true, true>"}
+# the sources each workload's kernel is built from (a change to any of them
+# makes that workload's committed counters stale)
+SOURCES_OF = {"c1": ("device_common.h", "nvfp4_kernels.h"),
+              "c2": ("device_common.h", "nvfp4_kernels.h"),
+              "c3": ("device_common.h", "nvfp4_kernels.h", "nvfp4_2d_kernels.h"),
+              "c4": ("device_common.h", "nvfp4_kernels.h"),
+              "c5": ("device_common.h", "mx_kernels.h"),
+              "f1": ("device_common.h", "nvfp4_kernels.h", "msed_kernels.h"),
+              "f2": ("device_common.h", "nvfp4_kernels.h", "rows_kernels.h"),
+              "f3": ("device_common.h", "mxgemm_kernels.h"),
+              "f4a": ("device_common.h", "nvfp4_kernels.h", "requant_kernels.h"),
+              "f4g": ("device_common.h", "nvfp4_kernels.h", "requant_kernels.h")}
 METRIC = "NVFP4 4/6 quantize GB/s (bf16 in + fp4/scale out) and % of HBM peak"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "nvfp4_4o6_8192x4096_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_by_workload.json")
 
 # workload -> (rows, cols, kind, flags, label)
 ROWS = {
@@ -71,7 +100,6 @@ ROWS = {
 # workload -> the seeded tensor it quantizes, where that is another workload's
 DATA_OF = {"f1": "c4", "f2": "c2", "f3": "c5"}
 GEMM_N = 8192                                   # f3: B^T rows (N); K = the tensor's cols
-MFMA_FP4_PEAK_TFLOPS = 10100.0                  # dense FP4 matrix peak of MI355X
 # requant workload -> (workload whose quantization is the input, its flags)
 REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
 SEED = 0x0123456789ABCDEF
@@ -80,8 +108,8 @@ SEED = 0x0123456789ABCDEF
 def algorithmic_bytes(wl):
     rows, cols, kind, flags, _ = ROWS[wl]
     n = rows * cols
-    if kind == "gemm":                               # operands in, fp32 C out
-        return rows * cols // 2 + rows * cols // 32 + 2 * (GEMM_N * cols // 2 + GEMM_N * cols // 32) \
+    if kind == "gemm":                               # A and B^T (codes + scales) in, fp32 C out
+        return (rows * cols // 2 + rows * cols // 32) + (GEMM_N * cols // 2 + GEMM_N * cols // 32) \
             + 4 * rows * GEMM_N
     if kind == "requant":                            # NVFP4 in, NVFP4 of the transpose out
         return 2 * (n // 2 + n // 16 + 4)
@@ -97,29 +125,43 @@ def algorithmic_bytes(wl):
     return 2 * n + n // 2 + n // 16 + 4
 
 
-# the sources the 1D quantize kernel (the one the counters measure) is built from
-COUNTED_SOURCES = ("device_common.h", "nvfp4_kernels.h")
-
-
-def kernel_source_sha():
+def sources_sha(wl):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_reduce_amd", "csrc")
-    for f in COUNTED_SOURCES:
+    for f in SOURCES_OF[wl]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the 4/6 quantize kernel from the committed
-    rocprofv3 counter summary, or None when it is missing or stale."""
+def counters_of(wl):
+    """Per-launch rocprofv3 figures of the workload's kernel from the
+    committed summary, or None when missing or taken on other sources."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     with open(COUNTERS_FILE) as f:
-        p = json.load(f)
-    if p.get("kernel_source_sha") != kernel_source_sha():
+        p = json.load(f).get(wl)
+    if not p or p.get("sources_sha") != sources_sha(wl):
         return None
-    return p.get("hbm_bytes_per_launch")
+    return p
+
+
+def roofline(wl, us):
+    """HBM and vector-ALU roofline of the workload's kernel at `us` per launch."""
+    alg = algorithmic_bytes(wl)
+    c = counters_of(wl) or {}
+    hbm = {"achieved": round(alg / us / 1e3, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)}
+    out = {"hbm": hbm, "traffic": c.get("hbm_bytes"),
+           "traffic_source": "rocprofv3 FETCH_SIZE + WRITE_SIZE (calibrated), " + COUNTERS_FILE[len(ROOT) + 1:]
+           if c.get("hbm_bytes") else None}
+    slots = c.get("valu_issue_slots")
+    if slots:
+        ach = slots / us / 1e3                        # G slots per second
+        out["valu"] = {"achieved": round(ach, 1), "peak": VALU_PEAK_GSLOTS,
+                       "unit": "G wave64 VALU issue slots/s", "frac": round(ach / VALU_PEAK_GSLOTS, 4),
+                       "issue_slots_per_launch": slots, "valu_insts_per_launch": c.get("valu_insts")}
+    return out
 
 
 # ------------------------------------------------------------------ GPU side
@@ -270,6 +312,8 @@ class Row:
 
 
 def time_loop(torch, stream, fn, steps, warmup):
+    """Mean ms per call of `steps` back-to-back calls (HIP events on the
+    launch stream around the whole run) and the host wall time."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -284,13 +328,27 @@ def time_loop(torch, stream, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_launches(torch, stream, fn, steps, warmup):
-    """Mean time per launch of a single-kernel call: HIP events on the launch
-    stream around `steps` back-to-back launches (so it includes the short
-    dispatch gap between consecutive kernels; rocprofv3's kernel duration
-    excludes it)."""
-    ms, _ = time_loop(torch, stream, fn, steps, warmup)
-    return ms
+def launch_stats(torch, stream, fn, n, warmup, batch=10):
+    """n calls: the mean of back-to-back calls (HIP events around the whole
+    run; it includes the short dispatch gap between consecutive kernels,
+    which rocprofv3's kernel duration excludes) and the median, p10 and p90
+    over n / batch batches of `batch` back-to-back calls (an event pair per
+    batch: an event recorded between every two calls would add several us
+    to each), as us per call."""
+    mean_ms, _ = time_loop(torch, stream, fn, n, warmup)
+    nb = max(1, n // batch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    ev[0].record(stream)
+    for b in range(nb):
+        for i in range(batch):
+            fn(b * batch + i)
+        ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[b].elapsed_time(ev[b + 1]) * 1e3 / batch for b in range(nb))
+    q = lambda f: per[min(nb - 1, int(round(f * (nb - 1))))]
+    return {"launches": n, "us_mean": round(mean_ms * 1e3, 3), "us_median": round(q(0.5), 3),
+            "us_p10": round(q(0.1), 3), "us_p90": round(q(0.9), 3),
+            "spread": "median/p10/p90 over %d batches of %d back-to-back calls" % (nb, batch)}
 
 
 CAL_BYTES = 2 * 8192 * 4096          # one 64 MiB int16 tensor
@@ -312,6 +370,44 @@ def copy_reference(torch, row):
 
 
 # ------------------------------------------------------------------ CPU side
+def cpu_info():
+    """Host share used for the CPU baseline: at most the threads this
+    process may run on, OMP_NUM_THREADS when set, and 16 (one GPU's share
+    of a GPU host)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0))
+    threads = aff
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        threads = min(threads, int(env))
+    return {"nproc": os.cpu_count(), "affinity": aff, "threads": min(threads, 16), "model": model}
+
+
+class CachedGen:
+    """synthetic.gen with the arrays kept: the CPU baseline and the GPU
+    rows quantize the same bytes without generating them twice."""
+
+    def __init__(self, synthetic):
+        self.s, self.cache = synthetic, {}
+
+    def gen(self, *a, **k):
+        key = (a, tuple(sorted(k.items())))
+        if key not in self.cache:
+            self.cache[key] = self.s.gen(*a, **k)
+        return self.cache[key]
+
+    def __getattr__(self, name):
+        return getattr(self.s, name)
+
+
 def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0, w_np=None):
     """The CPU oracle, as it stands (single-threaded C), on the workload or
     on its first max_rows rows; repeated until ~budget_s of work."""
@@ -359,12 +455,85 @@ def cpu_oracle(wl, x_np, max_rows=None, budget_s=10.0, w_np=None):
             "sample": "%s, %d runs, median %.2f s" % (what, len(times), med)}
 
 
+# worker-process state of the all-core oracle run (set before the fork)
+_MC = {}
+
+
+def _mc_amax(sl):
+    import oracle
+    return oracle.tensor_amax(_MC["x"][sl[0]:sl[1]], _MC["flags"], SEED)
+
+
+def _mc_quant(args):
+    import numpy as np
+    import oracle
+    (r0, r1), amax = args
+    q = oracle.nvfp4_quantize(_MC["x"][r0:r1], _MC["flags"], seed=SEED, amax=amax)
+    cols = _MC["x"].shape[1]
+    codes = np.ndarray((_MC["rows"], cols // 2), np.uint8, buffer=_MC["shm_c"].buf)
+    scales = np.ndarray((_MC["rows"], cols // 16), np.uint8, buffer=_MC["shm_s"].buf)
+    codes[r0:r1] = q["codes"]
+    scales[r0:r1] = q["scales"]
+    return float(q["alpha"])
+
+
+def cpu_oracle_all_cores(wl, x_np, threads, runs=3):
+    """The oracle on all `threads` host cores for a 1D NVFP4 workload without
+    SR (its SR counter is the element index in the whole tensor): rows split
+    over worker processes, first the tensor amax of each slice (the max over
+    slices is exact), then each slice quantized with that amax.  Results go
+    to shared memory and must equal the single-process oracle bit for bit.
+    Worker processes are forked before this process touches the GPU."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    import numpy as np
+    import oracle
+    oracle.build()
+    rows, cols, kind, flags, _ = ROWS[wl]
+    assert kind == "nvfp4" and not (flags & (2 | 8)), wl
+    shm_c = shared_memory.SharedMemory(create=True, size=rows * cols // 2)
+    shm_s = shared_memory.SharedMemory(create=True, size=rows * cols // 16)
+    try:
+        _MC.update(x=x_np, flags=flags, rows=rows, shm_c=shm_c, shm_s=shm_s)
+        step = -(-rows // threads)
+        slices = [(r, min(rows, r + step)) for r in range(0, rows, step)]
+        times = []
+        with mp.get_context("fork").Pool(threads) as pool:
+            pool.map(_mc_amax, slices)                       # start-up, untimed
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                amax = max(pool.map(_mc_amax, slices))
+                pool.map(_mc_quant, [(sl, amax) for sl in slices])
+                times.append(time.perf_counter() - t0)
+        want = oracle.nvfp4_quantize(x_np, flags, seed=SEED)
+        codes = np.ndarray((rows, cols // 2), np.uint8, buffer=shm_c.buf)
+        scales = np.ndarray((rows, cols // 16), np.uint8, buffer=shm_s.buf)
+        same = bool(np.array_equal(codes, want["codes"]) and np.array_equal(scales, want["scales"]))
+        del codes, scales
+    finally:
+        _MC.clear()
+        shm_c.close()
+        shm_c.unlink()
+        shm_s.close()
+        shm_s.unlink()
+    assert same, "all-core oracle differs from the single-process oracle"
+    med = sorted(times)[len(times) // 2]
+    return {"value": round(algorithmic_bytes(wl) / med / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "full %dx%d workload, rows split over %d processes (amax of each slice, "
+                      "then each slice quantized with the tensor amax; bit-identical to one "
+                      "process), %d runs, median %.3f s" % (rows, cols, threads, runs, med)}
+
+
 # ------------------------------------------------------------------ profile summaries
 def summarize(out_path, dirs, command):
     """Summarize rocprofv3 output directories (kernel trace and/or --pmc
-    FETCH_SIZE / WRITE_SIZE) into a short markdown file.  Traffic is scaled
-    by what the same counter reads for the plain 64 MiB copy the benchmark
-    runs (its true bytes are known)."""
+    counters) into a short markdown file, and merge the per-workload
+    figures (calibrated HBM bytes, VALU instructions and issue slots, mean
+    kernel time) into COUNTERS_FILE.  Traffic is scaled by what the same
+    counter reads for the plain 64 MiB bitwise-or the benchmark runs (its
+    true bytes are known)."""
     import glob
     import re
     import sqlite3
@@ -387,15 +556,20 @@ def summarize(out_path, dirs, command):
                     counters.setdefault((short(n), cn, g), []).append(v)
     lines = ["# rocprofv3 summary", "", "Command:", "", "```", command, "```", ""]
     if durations:
-        lines += ["| kernel | launches | avg us | median us | min us | max us |",
-                  "|---|---|---|---|---|---|"]
+        lines += ["| kernel | launches | avg us | median us | p10 us | p90 us | min us | max us |",
+                  "|---|---|---|---|---|---|---|---|"]
         for k, v in sorted(durations.items(), key=lambda kv: -sum(kv[1])):
-            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f |" % (
-                k, len(v), sum(v) / len(v), statistics.median(v), min(v), max(v)))
+            sv = sorted(v)
+            pq = lambda f: sv[min(len(sv) - 1, int(round(f * (len(sv) - 1))))]
+            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+                k, len(v), sum(v) / len(v), statistics.median(v), pq(0.1), pq(0.9), min(v), max(v)))
         lines.append("")
-    result = {}
+    merged = {}
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE) as f:
+            merged = json.load(f)
     if counters:
-        lines += ["| kernel | grid | counter | KiB per dispatch (mean) |", "|---|---|---|---|"]
+        lines += ["| kernel | grid | counter | mean per dispatch |", "|---|---|---|---|"]
         for (k, cn, g), v in sorted(counters.items()):
             lines.append("| %s | %d | %s | %.1f |" % (k, g, cn, sum(v) / len(v)))
         cal = {}
@@ -406,27 +580,50 @@ def summarize(out_path, dirs, command):
         if cal:
             lines += ["", "Calibration (64 MiB int16 bitwise-or: %d B read, %d B written): "
                       "FETCH_SIZE x %.3f, WRITE_SIZE x %.3f" % (
-                          CAL_BYTES, CAL_BYTES, cal.get("FETCH_SIZE", 0), cal.get("WRITE_SIZE", 0)),
-                      "", "| workload | kernel | fetched B | written B | total B | algorithmic B | ratio |",
-                      "|---|---|---|---|---|---|---|"]
-            for wl, kern in KERNEL_OF.items():
-                q = {cn: sum(v) / len(v) for (k, cn, g), v in counters.items() if k.startswith(kern)}
-                if not q:
-                    continue
-                fetch = q.get("FETCH_SIZE", 0) * 1024 * cal.get("FETCH_SIZE", 1)
-                write = q.get("WRITE_SIZE", 0) * 1024 * cal.get("WRITE_SIZE", 1)
-                alg = algorithmic_bytes(wl)
-                lines.append("| %s | %s | %.0f | %.0f | %.0f | %d | %.3f |" % (
-                    ROWS[wl][4], kern, fetch, write, fetch + write, alg, (fetch + write) / alg))
-                if wl == "c2":
-                    result = {"kernel_source_sha": kernel_source_sha(), "fetch_bytes": round(fetch),
-                              "write_bytes": round(write), "hbm_bytes_per_launch": round(fetch + write),
-                              "algorithmic_bytes": alg, "command": command}
+                          CAL_BYTES, CAL_BYTES, cal.get("FETCH_SIZE", 0), cal.get("WRITE_SIZE", 0))]
+        lines += ["", "| workload | kernel | fetched B | written B | total / algorithmic | "
+                  "VALU insts | VALU issue slots |", "|---|---|---|---|---|---|---|"]
+        for wl, kern in KERNEL_OF.items():
+            q = {}
+            for (k, cn, g), v in counters.items():
+                if k.startswith(kern):
+                    q.setdefault(cn, []).extend(v)
+            q = {cn: sum(v) / len(v) for cn, v in q.items()}
+            if not q:
+                continue
+            e = merged.get(wl, {})
+            if e.get("sources_sha") != sources_sha(wl):
+                e = {}
+            e.update(kernel=kern, sources_sha=sources_sha(wl), command=command)
+            raw = e.setdefault("raw", {})
+            raw.update({cn: round(v, 1) for cn, v in q.items()})
+            if "FETCH_SIZE" in q and "FETCH_SIZE" in cal:
+                e["fetch_bytes"] = round(q["FETCH_SIZE"] * 1024 * cal["FETCH_SIZE"])
+            if "WRITE_SIZE" in q and "WRITE_SIZE" in cal:
+                e["write_bytes"] = round(q["WRITE_SIZE"] * 1024 * cal["WRITE_SIZE"])
+            if "fetch_bytes" in e and "write_bytes" in e:
+                e["hbm_bytes"] = e["fetch_bytes"] + e["write_bytes"]
+            if "SQ_INSTS_VALU" in q:
+                e["valu_insts"] = round(q["SQ_INSTS_VALU"])
+            if "SQ_ACTIVE_INST_VALU" in q:            # units of 4 cycles of one SIMD
+                e["valu_issue_slots"] = round(q["SQ_ACTIVE_INST_VALU"])
+            if kern in durations:
+                e["avg_us_trace"] = round(sum(durations[kern]) / len(durations[kern]), 3)
+            merged[wl] = e
+            alg = algorithmic_bytes(wl)
+            lines.append("| %s | %s | %s | %s | %s | %s | %s |" % (
+                ROWS[wl][4], kern, e.get("fetch_bytes", "-"), e.get("write_bytes", "-"),
+                "%.3f" % (e["hbm_bytes"] / alg) if "hbm_bytes" in e else "-",
+                e.get("valu_insts", "-"), e.get("valu_issue_slots", "-")))
+    elif durations:
+        for wl, kern in KERNEL_OF.items():
+            if kern in durations and wl in merged and merged[wl].get("sources_sha") == sources_sha(wl):
+                merged[wl]["avg_us_trace"] = round(sum(durations[kern]) / len(durations[kern]), 3)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
-    if result:
+    if merged:
         with open(COUNTERS_FILE, "w") as f:
-            json.dump(result, f, indent=1)
+            json.dump(merged, f, indent=1, sort_keys=True)
     print("\n".join(lines))
 
 
@@ -434,10 +631,13 @@ def summarize(out_path, dirs, command):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timings")
     ap.add_argument("--no-rows", action="store_true", help="headline workload only")
+    ap.add_argument("--launches", type=int, default=MIN_LAUNCHES,
+                    help="launches per kernel-only figure (default %d; fewer only for "
+                         "profiler runs)" % MIN_LAUNCHES)
     ap.add_argument("--summarize", nargs="+", metavar=("OUT", "DIR"),
                     help="summarize rocprofv3 output directories into OUT")
     ap.add_argument("--command", default="", help="command recorded in a --summarize output")
@@ -451,19 +651,47 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    import synthetic as synthetic_mod
+    synthetic = CachedGen(synthetic_mod)
+    row_wls = () if args.no_rows else ("c1", "c3", "c4", "c5", "f1", "f2", "f3", "f4a", "f4g")
+
+    # CPU oracle first, before this process touches the GPU (its all-core
+    # run forks worker processes)
+    cpu = {}
+    if not args.no_cpu:
+        info = cpu_info()
+        x2 = synthetic.gen("c2")
+        single = cpu_oracle("c2", x2, budget_s=4.0)
+        cpu["baseline"] = dict(cpu_oracle_all_cores("c2", x2, info["threads"]),
+                               single_core=single, host=info)
+        for wl in row_wls:
+            _, _, kind, _, _ = ROWS[wl]
+            x = synthetic.gen(DATA_OF.get(wl, wl)) if kind != "requant" else \
+                synthetic.gen(REQUANT_SRC[wl][0])
+            w = synthetic.gen(DATA_OF[wl], GEMM_N, ROWS[wl][1], seed=4242) if kind == "gemm" else None
+            cpu[wl] = cpu_oracle(wl, x, max_rows=32 if kind == "gemm" else
+                                 (None if wl == "c1" else 512), budget_s=3.0, w_np=w)
+        print("cpu oracle done", flush=True)
+
     import torch
 
     import block_scaled_fp4_reduce_amd as fp4
-    import synthetic
 
     torch.cuda.set_device(0)
     head = Row("c2", fp4, torch, synthetic, np)
     ms_step, wall = time_loop(torch, head.stream, head.step, args.steps, args.warmup)
-    ms_kernel = time_launches(torch, head.stream, head.kernel, args.steps, args.warmup)
+    kst = launch_stats(torch, head.stream, head.kernel, args.launches, args.warmup)
+    sst = launch_stats(torch, head.stream, head.step, args.launches, args.warmup)
     copy_gbs = copy_reference(torch, head)
     alg = algorithmic_bytes("c2")
     value = alg / (ms_step * 1e-3) / 1e9
-    kernel_gbs = alg / (ms_kernel * 1e-3) / 1e9
+    rl = roofline("c2", kst["us_mean"])
+    fracs = {"hbm": rl["hbm"]["frac"]}
+    if "valu" in rl:
+        fracs["alu"] = rl["valu"]["frac"]
+    bound = max(fracs, key=fracs.get)
+    main_roof = rl["hbm"] if bound == "hbm" else rl["valu"]
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -478,49 +706,58 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": head.label + "_bf16", "rows": 8192, "cols": 4096,
+                   "input_dtype": "bf16", "compute_dtype": "f32",
                    "values": "Student-t(4) x per-column lognormal(0,1), bf16",
                    "flags": "FOUR_OVER_SIX", "amax": "computed in-step",
                    "global_batch": 1, "parallelism": "none"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "quantize_kernel": {"us_avg": round(ms_kernel * 1e3, 3), "gbs": round(kernel_gbs, 2),
-                            "note": "amax given: one kernel per call, mean over back-to-back launches"},
+        "step": dict(sst, gbs_mean=round(alg / sst["us_mean"] / 1e3, 1)),
+        "quantize_kernel": dict(kst, gbs_mean=round(alg / kst["us_mean"] / 1e3, 1),
+                                gbs_median=round(alg / kst["us_median"] / 1e3, 1),
+                                note="amax given: one kernel per call"),
+        "target_70pct_of_hbm": {"A_quantize_kernel_mean": rl["hbm"]["frac"] >= 0.7,
+                                "B_full_step": value / HBM_PEAK_GBS >= 0.7},
         "copy_kernel_gbs": round(copy_gbs, 1),
-        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profile()},
+        "roofline": {"bound": "alu" if bound == "alu" else "hbm",
+                     "achieved": main_roof["achieved"], "peak": main_roof["peak"],
+                     "unit": main_roof["unit"], "frac": main_roof["frac"],
+                     "traffic": rl["traffic"], "traffic_source": rl["traffic_source"],
+                     "hbm": rl["hbm"], "valu": rl.get("valu"),
+                     "kernel": KERNEL_OF["c2"], "algorithmic_bytes": alg},
         "wall_s": round(wall, 4),
     }
-    if not args.no_rows:
+    if row_wls:
         rows = []
-        for wl in ("c1", "c3", "c4", "c5", "f1", "f2", "f3", "f4a", "f4g"):
+        for wl in row_wls:
             r = Row(wl, fp4, torch, synthetic, np)
             st, _ = time_loop(torch, r.stream, r.step, max(10, args.steps // 2), 3)
-            kt = time_launches(torch, r.stream, r.kernel, max(10, args.steps // 2), 3)
+            ks = launch_stats(torch, r.stream, r.kernel, args.launches, 3)
             if r.kind == "gemm":
                 fl = 2.0 * r.rows * GEMM_N * r.cols
-                entry = {"workload": r.label, "flops": fl, "kernel_us": round(kt * 1e3, 3),
-                         "tflops": round(fl / (kt * 1e-3) / 1e12, 1),
-                         "kernel_frac_mfma_fp4": round(fl / (kt * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4)}
-                if not args.no_cpu:
-                    entry["cpu_oracle"] = cpu_oracle(wl, r.x_np, max_rows=32, budget_s=3.0, w_np=r.w_np)
-                rows.append(entry)
-                del r
-                torch.cuda.empty_cache()
-                continue
-            a = algorithmic_bytes(wl)
-            entry = {"workload": r.label, "algorithmic_bytes": a,
-                     "step_us": round(st * 1e3, 3), "step_gbs": round(a / (st * 1e-3) / 1e9, 1),
-                     "kernel_us": round(kt * 1e3, 3), "kernel_gbs": round(a / (kt * 1e-3) / 1e9, 1),
-                     "kernel_frac_hbm": round(a / (kt * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-            if not args.no_cpu:
-                entry["cpu_oracle"] = cpu_oracle(wl, r.x_np, max_rows=None if wl == "c1" else 512,
-                                                 budget_s=3.0)
+                tf = fl / ks["us_mean"] / 1e6
+                entry = {"workload": r.label, "flops": fl, "kernel": ks,
+                         "tflops": round(tf, 1), "kernel_frac_mfma_fp4": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
+                         "bound": "mfma", "hbm": roofline(wl, ks["us_mean"])["hbm"],
+                         "traffic": roofline(wl, ks["us_mean"])["traffic"]}
+            else:
+                a = algorithmic_bytes(wl)
+                rw = roofline(wl, ks["us_mean"])
+                fr = {"hbm": rw["hbm"]["frac"]}
+                if "valu" in rw:
+                    fr["alu"] = rw["valu"]["frac"]
+                entry = {"workload": r.label, "algorithmic_bytes": a,
+                         "step_us": round(st * 1e3, 3), "step_gbs": round(a / (st * 1e-3) / 1e9, 1),
+                         "kernel": ks, "kernel_gbs": round(a / ks["us_mean"] / 1e3, 1),
+                         "kernel_frac_hbm": rw["hbm"]["frac"], "bound": max(fr, key=fr.get),
+                         "valu": rw.get("valu"), "traffic": rw["traffic"]}
+            if wl in cpu:
+                entry["cpu_oracle"] = cpu[wl]
             rows.append(entry)
             del r
             torch.cuda.empty_cache()
         line["rows"] = rows
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_oracle("c2", head.x_np)
+    if cpu:
+        line["cpu_baseline"] = cpu["baseline"]
     print(json.dumps(line), flush=True)
 
 

@@ -5,6 +5,7 @@
 // (bias 7, max 448); UE8M0 power-of-two scales for MXFP4.
 #pragma once
 
+#include <tuple>
 #include <utility>
 
 #include <hip/hip_runtime.h>
@@ -13,6 +14,22 @@
 namespace fp4q {
 
 constexpr int kThreads = 256;             // 4 wave64s per workgroup
+
+// Host: launch `kernel` on `st` and return that launch's own status
+// (hipLaunchKernel's return value), so a failure left behind by an earlier,
+// unrelated HIP call of the caller is neither reported nor consumed.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), unsigned grid, unsigned block, hipStream_t st,
+                         A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  std::tuple<P...> args{static_cast<P>(a)...};
+  return std::apply(
+      [&](auto&... v) {
+        void* argv[] = {(void*)&v...};
+        return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(block), argv, 0, st);
+      },
+      args);
+}
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
 

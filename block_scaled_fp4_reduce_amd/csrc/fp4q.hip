@@ -50,7 +50,12 @@ int amax_groups(int64_t ngroups16) {
   return (int)g;
 }
 
-int launched() { return hipGetLastError() == hipSuccess ? FP4_OK : FP4_E_HIP; }
+// Status of the launches an entry point queued (each launch reports its own
+// result, see launch(); the thread's last-error state is never read).
+int launched(hipError_t e) { return e == hipSuccess ? FP4_OK : FP4_E_HIP; }
+
+// First failure of a sequence of launches.
+hipError_t first(hipError_t a, hipError_t b) { return a != hipSuccess ? a : b; }
 
 // Compute units of the current device (queried once per device; 256 on MI355X).
 int num_cus() {
@@ -67,29 +72,30 @@ int num_cus() {
 }
 
 // Queue the amax pass: partial maxima into ws (as uint32), `groups` of them.
-void launch_amax_partial(const uint16_t* x, int64_t ngroups16, uint32_t flags, uint64_t seed,
-                         uint32_t* ws, int groups, hipStream_t st) {
+hipError_t launch_amax_partial(const uint16_t* x, int64_t ngroups16, uint32_t flags,
+                               uint64_t seed, uint32_t* ws, int groups, hipStream_t st) {
   const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
   if (flags & FP4_RHT16)
-    amax_partial_kernel<true><<<groups, kAmaxThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
-  else
-    amax_partial_kernel<false><<<groups, kAmaxThreads, 0, st>>>((const uint4*)x, ngroups16, ws, lo, hi);
+    return launch(amax_partial_kernel<true>, groups, kAmaxThreads, st, (const uint4*)x, ngroups16,
+                  ws, lo, hi);
+  return launch(amax_partial_kernel<false>, groups, kAmaxThreads, st, (const uint4*)x, ngroups16,
+                ws, lo, hi);
 }
 
 template <bool F46, bool SR, bool RHT>
-void launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int namax,
-               float* alpha_out, uint8_t* codes, uint8_t* scales, uint8_t* choice,
-               uint64_t seed, hipStream_t st) {
+hipError_t launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, int namax,
+                     float* alpha_out, uint8_t* codes, uint8_t* scales, uint8_t* choice,
+                     uint64_t seed, hipStream_t st) {
   int64_t grid = nblocks > 0 ? cdiv(nblocks, (int64_t)kThreads) : 1;
   const int64_t resident = (int64_t)num_cus() * (SR ? kWgPerCu : kWgPerCuNoSr);
   if (grid > resident) grid = resident;
-  nvfp4_1d_kernel<F46, SR, RHT><<<(unsigned)grid, kThreads, 0, st>>>(
-      (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
-      (uint32_t)seed, (uint32_t)(seed >> 32));
+  return launch(nvfp4_1d_kernel<F46, SR, RHT>, (unsigned)grid, kThreads, st, (const uint4*)x,
+                nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice, (uint32_t)seed,
+                (uint32_t)(seed >> 32));
 }
 
 template <bool F46, bool SR, bool RHT>
-void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* alpha, int64_t rows,
+hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const float* alpha, int64_t rows,
                     int64_t cols, const float* amax_in, uint32_t* ws, float* alpha_out,
                     uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t, uint64_t seed,
                     hipStream_t st) {
@@ -106,16 +112,17 @@ void launch_requant(const uint8_t* codes, const uint8_t* scales, const float* al
   const int64_t resident = (int64_t)num_cus() * kRqWgPerCu;
   const uint32_t* abits = (const uint32_t*)amax_in;
   int namax = 1;
+  hipError_t e = hipSuccess;
   if (!amax_in) {
     const int64_t ga = grid(resident < kRqAmaxGroups ? resident : kRqAmaxGroups);
-    rq_amax_kernel<RHT><<<(unsigned)ga, kRqThreads, 0, st>>>(codes, scales, alpha, rows, cols, TY,
-                                                            TX, ws, lo, hi);
+    e = launch(rq_amax_kernel<RHT>, (unsigned)ga, kRqThreads, st, codes, scales, alpha, rows,
+               cols, TY, TX, ws, lo, hi);
     abits = ws;
     namax = (int)ga;
   }
-  rq_quant_kernel<F46, SR, RHT><<<(unsigned)grid(resident), kRqThreads, 0, st>>>(
-      codes, scales, alpha, rows, cols, TY, TX, abits, namax, alpha_out,
-      codes_t, scales_t, choice_t, lo, hi);
+  return first(e, launch(rq_quant_kernel<F46, SR, RHT>, (unsigned)grid(resident), kRqThreads, st,
+                         codes, scales, alpha, rows, cols, TY, TX, abits, namax, alpha_out,
+                         codes_t, scales_t, choice_t, lo, hi));
 }
 
 // Persistent grid: as many workgroups of `kernel` as fit on the chip at
@@ -135,25 +142,26 @@ int64_t resident_grid(const void* kernel, int& per_cu, int64_t want) {
 }
 
 template <bool F46, bool SR, bool RHT, int NB>
-void launch_rows_wave(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
-                      uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
-                      hipStream_t st) {
+hipError_t launch_rows_wave(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                            uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                            hipStream_t st) {
   static int per_cu = 0;
   const int64_t grid = resident_grid((const void*)nvfp4_rows_kernel<F46, SR, RHT, NB>, per_cu,
                                      cdiv(rows, kRowWaves));
-  nvfp4_rows_kernel<F46, SR, RHT, NB><<<(unsigned)grid, kRowThreads, 0, st>>>(
-      x, rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return launch(nvfp4_rows_kernel<F46, SR, RHT, NB>, (unsigned)grid, kRowThreads, st, x, rows,
+                cols, alpha_rows, codes, scales, choice, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
 template <bool F46, bool SR, bool RHT, int NB, bool ONE>
-void launch_rows_wg(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
-                    uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
-                    hipStream_t st) {
+hipError_t launch_rows_wg(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                          uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                          hipStream_t st) {
   static int per_cu = 0;
   const int64_t grid =
       resident_grid((const void*)nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, per_cu, rows);
-  nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE><<<(unsigned)grid, kRowThreads, 0, st>>>(
-      x, rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return launch(nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, (unsigned)grid, kRowThreads, st, x,
+                rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed,
+                (uint32_t)(seed >> 32));
 }
 
 // Rows of up to 128 blocks: one wave per row (1 or 2 blocks per lane).
@@ -161,22 +169,18 @@ void launch_rows_wg(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_
 // registers (rows up to 16384 values are read once); beyond that two
 // sweeps over the row, the second from cache.
 template <bool F46, bool SR, bool RHT>
-void launch_rows(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
-                 uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
-                 hipStream_t st) {
+hipError_t launch_rows(const uint16_t* x, int64_t rows, int64_t cols, float* alpha_rows,
+                       uint8_t* codes, uint8_t* scales, uint8_t* choice, uint64_t seed,
+                       hipStream_t st) {
   const int64_t nblk = cols / 16;
-  if (nblk <= 64)
-    launch_rows_wave<F46, SR, RHT, 1>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
-  else if (nblk <= 128)
-    launch_rows_wave<F46, SR, RHT, 2>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
-  else if (nblk <= 256)
-    launch_rows_wg<F46, SR, RHT, 1, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
-  else if (nblk <= 512)
-    launch_rows_wg<F46, SR, RHT, 2, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
-  else if (nblk <= 1024)
-    launch_rows_wg<F46, SR, RHT, 4, true>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
-  else
-    launch_rows_wg<F46, SR, RHT, 4, false>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st);
+#define FP4Q_ARGS x, rows, cols, alpha_rows, codes, scales, choice, seed, st
+  if (nblk <= 64) return launch_rows_wave<F46, SR, RHT, 1>(FP4Q_ARGS);
+  if (nblk <= 128) return launch_rows_wave<F46, SR, RHT, 2>(FP4Q_ARGS);
+  if (nblk <= 256) return launch_rows_wg<F46, SR, RHT, 1, true>(FP4Q_ARGS);
+  if (nblk <= 512) return launch_rows_wg<F46, SR, RHT, 2, true>(FP4Q_ARGS);
+  if (nblk <= 1024) return launch_rows_wg<F46, SR, RHT, 4, true>(FP4Q_ARGS);
+  return launch_rows_wg<F46, SR, RHT, 4, false>(FP4Q_ARGS);
+#undef FP4Q_ARGS
 }
 
 }  // namespace
@@ -217,15 +221,20 @@ int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flag
   hipStream_t st = (hipStream_t)stream;
   const int64_t ng = n / 16;
   const int groups = amax_groups(ng);
-  launch_amax_partial(x, ng, flags, seed, (uint32_t*)ws, groups, st);
-  amax_finalize_kernel<<<1, kThreads, 0, st>>>((const uint32_t*)ws, groups, amax_out);
-  return launched();
+  const hipError_t e = launch_amax_partial(x, ng, flags, seed, (uint32_t*)ws, groups, st);
+  return launched(first(e, launch(amax_finalize_kernel, 1, kThreads, st, (const uint32_t*)ws,
+                                  groups, amax_out)));
 }
 
-int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
-                   const float* amax_in, float* alpha_out, uint8_t* codes, uint8_t* scales,
-                   uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t, void* ws,
-                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of nvfp4_quantize.
+int check_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                         const float* amax_in, const float* alpha_out, const uint8_t* codes,
+                         const uint8_t* scales, const uint8_t* codes_t, const uint8_t* scales_t,
+                         const void* ws, size_t ws_bytes) {
   const int64_t n = rows * cols;
   const bool two_d = (flags & FP4_BLOCK2D) != 0;
   const bool want_t = two_d && (flags & FP4_COLWISE);
@@ -241,44 +250,58 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
       !aligned(ws, 4) || (want_t && !aligned(codes_t, 16)))
     return FP4_E_ALIGN;
   if (!amax_in && ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
+  return FP4_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                   const float* amax_in, float* alpha_out, uint8_t* codes, uint8_t* scales,
+                   uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (int rc = check_nvfp4_quantize(x, rows, cols, flags, amax_in, alpha_out, codes, scales,
+                                    codes_t, scales_t, ws, ws_bytes))
+    return rc;
+  const int64_t n = rows * cols;
+  const bool two_d = (flags & FP4_BLOCK2D) != 0;
+  const bool want_t = two_d && (flags & FP4_COLWISE);
   hipStream_t st = (hipStream_t)stream;
   const int64_t nblocks = n / 16;
   const uint32_t* abits = (const uint32_t*)amax_in;
   int namax = 1;
+  hipError_t e = hipSuccess;
   if (!amax_in) {
     namax = amax_groups(nblocks);
-    launch_amax_partial(x, nblocks, flags, seed, (uint32_t*)ws, namax, st);
+    e = launch_amax_partial(x, nblocks, flags, seed, (uint32_t*)ws, namax, st);
     abits = (const uint32_t*)ws;
   }
   if (two_d) {
     const bool f46 = (flags & FP4_FOUR_OVER_SIX) != 0;
-    launch_nvfp4_2d(x, rows, cols, f46, abits, namax, alpha_out, codes, scales, choice,
-                    want_t ? codes_t : nullptr, want_t ? scales_t : nullptr, st, num_cus());
-    return launched();
+    return launched(first(e, launch_nvfp4_2d(x, rows, cols, f46, abits, namax, alpha_out, codes,
+                                             scales, choice, want_t ? codes_t : nullptr,
+                                             want_t ? scales_t : nullptr, st, num_cus())));
   }
   if (flags & FP4_MSEDEN) {              // always with RHT16 (checked above)
     int64_t grid = nblocks > 0 ? cdiv(nblocks, (int64_t)kThreads) : 1;
     if (grid > (int64_t)num_cus() * kWgPerCu) grid = (int64_t)num_cus() * kWgPerCu;
-    nvfp4_msed_kernel<true><<<(unsigned)grid, kThreads, 0, st>>>(
-        (const uint4*)x, nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice,
-        (uint32_t)seed, (uint32_t)(seed >> 32));
-    return launched();
+    return launched(first(e, launch(nvfp4_msed_kernel<true>, (unsigned)grid, kThreads, st,
+                                    (const uint4*)x, nblocks, abits, namax, alpha_out,
+                                    (uint2*)codes, scales, choice, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32))));
   }
   const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
-  if (f46 && rht)
-    launch_1d<true, false, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  else if (f46)
-    launch_1d<true, false, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  else if (sr && rht)
-    launch_1d<false, true, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  else if (sr)
-    launch_1d<false, true, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  else if (rht)
-    launch_1d<false, false, true>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  else
-    launch_1d<false, false, false>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st);
-  return launched();
+#define FP4Q_1D(F, S, R) \
+  launch_1d<F, S, R>(x, nblocks, abits, namax, alpha_out, codes, scales, choice, seed, st)
+  if (f46 && rht) e = first(e, FP4Q_1D(true, false, true));
+  else if (f46) e = first(e, FP4Q_1D(true, false, false));
+  else if (sr && rht) e = first(e, FP4Q_1D(false, true, true));
+  else if (sr) e = first(e, FP4Q_1D(false, true, false));
+  else if (rht) e = first(e, FP4Q_1D(false, false, true));
+  else e = first(e, FP4Q_1D(false, false, false));
+#undef FP4Q_1D
+  return launched(e);
 }
 
 int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,
@@ -303,14 +326,15 @@ int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float*
 #define FP4Q_RQ(F, S, R)                                                                     \
   launch_requant<F, S, R>(codes, scales, alpha, rows, cols, amax_in, w, alpha_out, codes_t, \
                           scales_t, choice_t, seed, st)
-  if (f46 && rht) FP4Q_RQ(true, false, true);
-  else if (f46) FP4Q_RQ(true, false, false);
-  else if (sr && rht) FP4Q_RQ(false, true, true);
-  else if (sr) FP4Q_RQ(false, true, false);
-  else if (rht) FP4Q_RQ(false, false, true);
-  else FP4Q_RQ(false, false, false);
+  hipError_t e;
+  if (f46 && rht) e = FP4Q_RQ(true, false, true);
+  else if (f46) e = FP4Q_RQ(true, false, false);
+  else if (sr && rht) e = FP4Q_RQ(false, true, true);
+  else if (sr) e = FP4Q_RQ(false, true, false);
+  else if (rht) e = FP4Q_RQ(false, false, true);
+  else e = FP4Q_RQ(false, false, false);
 #undef FP4Q_RQ
-  return launched();
+  return launched(e);
 }
 
 int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -328,14 +352,15 @@ int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint32_t 
   const bool f46 = flags & FP4_FOUR_OVER_SIX, sr = flags & FP4_SR, rht = flags & FP4_RHT16;
 #define FP4Q_ROWS(F, S, R) \
   launch_rows<F, S, R>(x, rows, cols, alpha_rows, codes, scales, choice, seed, st)
-  if (f46 && rht) FP4Q_ROWS(true, false, true);
-  else if (f46) FP4Q_ROWS(true, false, false);
-  else if (sr && rht) FP4Q_ROWS(false, true, true);
-  else if (sr) FP4Q_ROWS(false, true, false);
-  else if (rht) FP4Q_ROWS(false, false, true);
-  else FP4Q_ROWS(false, false, false);
+  hipError_t e;
+  if (f46 && rht) e = FP4Q_ROWS(true, false, true);
+  else if (f46) e = FP4Q_ROWS(true, false, false);
+  else if (sr && rht) e = FP4Q_ROWS(false, true, true);
+  else if (sr) e = FP4Q_ROWS(false, true, false);
+  else if (rht) e = FP4Q_ROWS(false, false, true);
+  else e = FP4Q_ROWS(false, false, false);
 #undef FP4Q_ROWS
-  return launched();
+  return launched(e);
 }
 
 int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -352,10 +377,9 @@ int mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   if (!aligned(x, 16) || (rw && !aligned(codes_r, 16)) || (cw && !aligned(codes_c, 16)))
     return FP4_E_ALIGN;
   if (n == 0) return FP4_OK;
-  launch_mxfp4(x, rows, cols, (flags & FP4_HAD32) != 0, rw ? codes_r : nullptr,
-               rw ? scales_r : nullptr, cw ? codes_c : nullptr, cw ? scales_c : nullptr,
-               (hipStream_t)stream, num_cus());
-  return launched();
+  return launched(launch_mxfp4(x, rows, cols, (flags & FP4_HAD32) != 0, rw ? codes_r : nullptr,
+                              rw ? scales_r : nullptr, cw ? codes_c : nullptr,
+                              cw ? scales_c : nullptr, (hipStream_t)stream, num_cus()));
 }
 
 int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* bt_codes,
@@ -377,14 +401,13 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
   if (K == 0) {                           // empty sum: C = 0
     int64_t grid = cdiv(M * N, 256);
     if (grid > 4096) grid = 4096;
-    fill_zero_kernel<<<(unsigned)grid, 256, 0, (hipStream_t)stream>>>(c, M * N);
-    return launched();
+    return launched(launch(fill_zero_kernel, (unsigned)grid, 256, (hipStream_t)stream, c, M * N));
   }
   const int64_t tiles_m = cdiv(M, kGemmBM), tiles_n = cdiv(N, kGemmBN);
   const int64_t slots = xcd_grid(tiles_m, tiles_n, kGemmSuperY, kGemmSuperX);
-  mxfp4_gemm_kernel<<<(unsigned)slots, kGemmThreads, 0, (hipStream_t)stream>>>(
-      a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, (uint32_t)tiles_m, (uint32_t)tiles_n);
-  return launched();
+  return launched(launch(mxfp4_gemm_kernel, (unsigned)slots, kGemmThreads, (hipStream_t)stream,
+                         a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, (uint32_t)tiles_m,
+                         (uint32_t)tiles_n));
 }
 
 int fp4_dequantize(int format, const uint8_t* codes, const uint8_t* scales, const float* alpha,
@@ -407,14 +430,13 @@ int fp4_dequantize(int format, const uint8_t* codes, const uint8_t* scales, cons
   hipStream_t st = (hipStream_t)stream;
   if (format == FP4_FORMAT_NVFP4) {
     const int64_t nb = n / 16;
-    nvfp4_dequant_kernel<<<(unsigned)cdiv(nb, kThreads), kThreads, 0, st>>>(
-        (const uint2*)codes, scales, alpha, nb, cols / 16, two_d, (float4*)out);
-  } else {
-    const int64_t ng = n / 32;
-    mxfp4_dequant_kernel<<<(unsigned)cdiv(ng, kThreads), kThreads, 0, st>>>(
-        (const uint4*)codes, scales, ng, (float4*)out);
+    return launched(launch(nvfp4_dequant_kernel, (unsigned)cdiv(nb, kThreads), kThreads, st,
+                           (const uint2*)codes, scales, alpha, nb, cols / 16, two_d,
+                           (float4*)out));
   }
-  return launched();
+  const int64_t ng = n / 32;
+  return launched(launch(mxfp4_dequant_kernel, (unsigned)cdiv(ng, kThreads), kThreads, st,
+                         (const uint4*)codes, scales, ng, (float4*)out));
 }
 
 }  // extern "C"

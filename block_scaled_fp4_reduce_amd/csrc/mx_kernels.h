@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kMxThreads) void mxfp4_kernel(
   }
 }
 
-inline void launch_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, bool had,
+inline hipError_t launch_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, bool had,
                          uint8_t* codes_r, uint8_t* scales_r, uint8_t* codes_c,
                          uint8_t* scales_c, hipStream_t st, int num_cus) {
   const int64_t nslots = xcd_grid((rows + kMxRegion - 1) / kMxRegion,
@@ -347,18 +347,17 @@ inline void launch_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, bool had
   if (grid > nslots) grid = nslots;
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   const bool rw = codes_r != nullptr, cw = codes_c != nullptr;
-#define FP4Q_MX(H, R, C)                                                                     \
-  mxfp4_kernel<H, R, C><<<(unsigned)grid, kMxThreads, 0, st>>>(x, rows, cols, codes_r, scales_r, \
-                                                                codes_c, scales_c)
+#define FP4Q_MX(H, R, C)                                                                  \
+  launch(mxfp4_kernel<H, R, C>, (unsigned)grid, kMxThreads, st, x, rows, cols, codes_r, \
+         scales_r, codes_c, scales_c)
   if (had) {
-    if (rw && cw) FP4Q_MX(true, true, true);
-    else if (rw) FP4Q_MX(true, true, false);
-    else FP4Q_MX(true, false, true);
-  } else {
-    if (rw && cw) FP4Q_MX(false, true, true);
-    else if (rw) FP4Q_MX(false, true, false);
-    else FP4Q_MX(false, false, true);
+    if (rw && cw) return FP4Q_MX(true, true, true);
+    if (rw) return FP4Q_MX(true, true, false);
+    return FP4Q_MX(true, false, true);
   }
+  if (rw && cw) return FP4Q_MX(false, true, true);
+  if (rw) return FP4Q_MX(false, true, false);
+  return FP4Q_MX(false, false, true);
 #undef FP4Q_MX
 }
 

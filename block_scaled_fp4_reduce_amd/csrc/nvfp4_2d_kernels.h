@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   }
 }
 
-inline void launch_nvfp4_2d(const uint16_t* x, int64_t rows, int64_t cols, bool f46,
+inline hipError_t launch_nvfp4_2d(const uint16_t* x, int64_t rows, int64_t cols, bool f46,
                             const uint32_t* abits, int namax, float* alpha_out, uint8_t* codes,
                             uint8_t* scales, uint8_t* choice, uint8_t* codes_t,
                             uint8_t* scales_t, hipStream_t st, int num_cus) {
@@ -274,13 +274,13 @@ inline void launch_nvfp4_2d(const uint16_t* x, int64_t rows, int64_t cols, bool 
   grid = (grid + kXcds - 1) / kXcds * kXcds;
   if (grid < 1) grid = 1;
   const bool tr = codes_t != nullptr;
-#define FP4Q_2D(F, T)                                                                   \
-  nvfp4_2d_kernel<F, T><<<(unsigned)grid, kThreads, 0, st>>>(                           \
-      x, rows, cols, abits, namax, alpha_out, codes, scales, choice, codes_t, scales_t)
-  if (f46 && tr) FP4Q_2D(true, true);
-  else if (f46) FP4Q_2D(true, false);
-  else if (tr) FP4Q_2D(false, true);
-  else FP4Q_2D(false, false);
+#define FP4Q_2D(F, T)                                                                     \
+  launch(nvfp4_2d_kernel<F, T>, (unsigned)grid, kThreads, st, x, rows, cols, abits, namax, \
+         alpha_out, codes, scales, choice, codes_t, scales_t)
+  if (f46 && tr) return FP4Q_2D(true, true);
+  if (f46) return FP4Q_2D(true, false);
+  if (tr) return FP4Q_2D(false, true);
+  return FP4Q_2D(false, false);
 #undef FP4Q_2D
 }
 

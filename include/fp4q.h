@@ -34,8 +34,10 @@
  *    are E4M3 (bias 7, max 448), MXFP4 scales are UE8M0 (2^(code-127)).
  *  - Errors: the return value is an fp4_status.  Argument checks run on the
  *    host before any HIP call, so a rejected call touches no device state.
- *    FP4_E_HIP reports a failed kernel launch (hipGetLastError); faults
- *    during execution surface at the caller's next synchronisation.
+ *    FP4_E_HIP reports a failed kernel launch (the launch's own return
+ *    status; an error left by an earlier, unrelated HIP call is neither
+ *    reported nor cleared); faults during execution surface at the caller's
+ *    next synchronisation.
  *  - Tensors holding Inf/NaN, or (NVFP4) whose largest magnitude is below
  *    2^-64 without being zero, are outside the method's domain: the call
  *    succeeds and never faults, but codes and scales are unspecified.
@@ -143,7 +145,13 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
  *   alpha_rows [rows] device floats.
  *   codes      [rows][cols/2];  scales [rows][cols/16];  choice NULL or
  *              [rows][cols/16].
- *   Shapes: cols % 16 == 0.  No workspace. */
+ *   Shapes: cols % 16 == 0.  No workspace.
+ *   Domain, per row: a row whose largest magnitude (after RHT16) is not
+ *   zero but below 2^-64 (e.g. a row of bf16 subnormals) is outside the
+ *   method's domain, as a whole tensor with that amax would be: its codes,
+ *   scales and choice are unspecified (its alpha_rows entry is still
+ *   amax_r / (6*C)).  The other rows are unaffected and the call never
+ *   faults. */
 int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols,
                         uint32_t flags, uint64_t seed, float* alpha_rows,
                         uint8_t* codes, uint8_t* scales, uint8_t* choice,

@@ -19,6 +19,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fp4_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt copy of this same source to load instead (the sanitizer test
+# builds one with -fsanitize=address,undefined); never rebuilt here.
+_LIB_OVERRIDE = os.environ.get("FP4Q_ORACLE_LIB")
 
 FOUR_OVER_SIX = 1 << 0
 SR = 1 << 1
@@ -46,11 +49,17 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def loaded_path() -> str:
+    """Path of the oracle library lib() loads."""
+    return _LIB_OVERRIDE or _LIB
+
+
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(_LIB)
+        if not _LIB_OVERRIDE:
+            build()
+        L = C.CDLL(loaded_path())
         u8p, f32p, u16p, u32p = (C.POINTER(C.c_uint8), C.POINTER(C.c_float),
                                  C.POINTER(C.c_uint16), C.POINTER(C.c_uint32))
         L.orc_e2m1_encode.restype = C.c_uint8

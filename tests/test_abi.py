@@ -171,3 +171,4 @@ def test_empty_tensors_need_no_buffers(L):
     # zero-sized MX and dequant calls succeed without launching anything
     assert L.mxfp4_quantize(None, 0, 64, fp4.ROWWISE, None, None, None, None, None) == OK
     assert L.fp4_dequantize(1, None, None, None, 0, 64, 0, None, None) == OK
+

@@ -82,6 +82,44 @@ def test_gemm_of_quantizer_outputs(flags):
     check(qa["codes_r"], qa["scales_r"], qb["codes_c"], qb["scales_c"], "quantized")
 
 
+# Multi-tile grids in the launch configuration of the large products: the
+# super-tile order of the tile scheduler is on once the 256 x 256 tiles form
+# at least 8 groups of 4 x 8 tiles (M = 2048, N = 8192: 8 x 32 tiles); the
+# ragged case has a partial last row and column of tiles, the deep-K cases
+# 64 steps of K (and 48 with the super-tile order).
+@pytest.mark.parametrize("shape", [(2048, 8192, 1024), (2100, 8320, 512), (512, 512, 8192),
+                                   (2304, 8448, 6144)])
+def test_gemm_multitile(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M + 5 * N + 11 * K)
+    ac, asc = random_mx(M, K, rng)
+    bc, bsc = random_mx(N, K, rng)
+    check(ac, asc, bc, bsc, "multi-tile")
+
+
+def test_gemm_full_size_sampled():
+    """The benchmarked 16384 x 8192 x 8192 product, every output column, on
+    rows sampled from each 256-row tile (C[i, :] depends only on A's row i
+    and all of B, so the oracle computes just those rows)."""
+    M, N, K = 16384, 8192, 8192
+    rng = np.random.default_rng(16384)
+    ac, asc = random_mx(M, K, rng)
+    bc, bsc = random_mx(N, K, rng)
+    print("gemm case full size sampled", (M, N, K), flush=True)
+    got = fp4.mxfp4_gemm(u8(ac), u8(asc), u8(bc), u8(bsc))
+    torch.cuda.synchronize()
+    tiles = np.arange(0, M, 256)
+    rows = np.unique(np.concatenate([tiles + (tiles * 37) % 256, tiles + 255 - (tiles * 11) % 256,
+                                     [0, M - 1]]))
+    got = got[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    A = O.dequantize(1, ac[rows], asc[rows], 0.0, len(rows), K).astype(np.float64)
+    B = O.dequantize(1, bc, bsc, 0.0, N, K).astype(np.float64)
+    want = A @ B.T
+    bound = K * 2.0 ** -23 * (np.abs(A) @ np.abs(B).T) + 1e-30
+    err = np.abs(got - want)
+    assert np.all(err <= bound), "full size: %d sampled entries out of bound" % int((err > bound).sum())
+
+
 def test_gemm_edges():
     rng = np.random.default_rng(3)
     ac, asc = random_mx(64, 128, rng)

@@ -84,3 +84,25 @@ def test_rows_with_one_amax_match_the_per_tensor_quantizer():
     torch.cuda.synchronize()
     assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["scales"], b["scales"])
     assert torch.all(a["alpha"] == b["alpha"][0])
+
+
+@pytest.mark.parametrize("flags", [0, fp4.FOUR_OVER_SIX, fp4.RHT16 | fp4.SR])
+def test_rows_outside_the_domain_leave_the_others_exact(flags):
+    """Rows whose largest magnitude is non-zero but below 2^-64 (bf16
+    subnormals; normals near 2^-80) are outside the domain: the call must
+    succeed, and every other row (a zero row included) must still equal the
+    oracle bit for bit."""
+    rng = np.random.default_rng(5)
+    x = S.gen("c2", 24, 4096)
+    x[5] = (rng.integers(1, 0x80, 4096) | (rng.integers(0, 2, 4096) << 15)).astype(np.uint16)
+    x[9] = S.f32_to_bf16_bits((rng.standard_normal(4096) * 2.0 ** -80).astype(np.float32))
+    x[13] = 0
+    print("rows case out of domain", flags, flush=True)
+    got = fp4.nvfp4_quantize_rows(dev(x), flags, seed=SEED, want_choice=True)
+    torch.cuda.synchronize()
+    want = O.nvfp4_quantize_rows(x, flags, seed=SEED)
+    keep = np.setdiff1d(np.arange(24), [5, 9])
+    for k in ("codes", "scales") + (("choice",) if flags & fp4.FOUR_OVER_SIX else ()):
+        assert np.array_equal(got[k].cpu().numpy()[keep], want[k][keep]), k
+    ga = got["alpha"].cpu().numpy()[:24]
+    assert np.array_equal(ga, want["alpha"])           # alpha_r = amax_r / (6 C) on every row
