@@ -33,7 +33,8 @@ FORMAT_MXFP4 = 1
 STATUS = {0: "FP4_OK", -1: "FP4_E_NULL", -2: "FP4_E_SHAPE", -3: "FP4_E_ALIGN",
           -4: "FP4_E_FLAGS", -5: "FP4_E_WORKSPACE", -6: "FP4_E_HIP"}
 
-EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_quantize_rows",
+EXPORTS = ("fp4_workspace_bytes", "fp4_tensor_amax", "nvfp4_quantize", "nvfp4_quantize_noalloc",
+           "nvfp4_quantize_rows",
            "nvfp4_requantize_t", "mxfp4_quantize", "mxfp4_gemm", "fp4_dequantize",
            "fp4_status_str", "fp4_abi_version")
 
@@ -64,6 +65,8 @@ def lib():
         L.fp4_tensor_amax.argtypes = [vp, i64, i64, u32, u64, vp, vp, sz, vp]
         L.nvfp4_quantize.restype = C.c_int
         L.nvfp4_quantize.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.nvfp4_quantize_noalloc.restype = C.c_int
+        L.nvfp4_quantize_noalloc.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp, vp, vp, vp]
         L.nvfp4_quantize_rows.restype = C.c_int
         L.nvfp4_quantize_rows.argtypes = [vp, i64, i64, u32, u64, vp, vp, vp, vp, vp]
         L.nvfp4_requantize_t.restype = C.c_int
@@ -175,6 +178,22 @@ def nvfp4_quantize(x, flags=0, seed=0, amax=None, want_choice=False, ws=None, st
         o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o.get("choice")),
         _ptr(o.get("codes_t")), _ptr(o.get("scales_t")), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+    return o
+
+
+def nvfp4_quantize_noalloc(x, flags=0, seed=0, amax=None, out=None, stream=None):
+    """nvfp4_quantize without a workspace: the library keeps the amax pass's
+    partial maxima in its own fixed device array.  ``out`` must hold every
+    output buffer (``codes``, ``scales``, ``alpha``, optional ``choice``,
+    ``codes_t``/``scales_t`` for BLOCK2D|COLWISE): this call allocates
+    nothing.  Calls overlapping on one device race (see include/fp4q.h)."""
+    xb = _as_bits(x)
+    rows, cols = xb.shape
+    o = out
+    _check("nvfp4_quantize_noalloc", lib().nvfp4_quantize_noalloc(
+        xb.data_ptr(), rows, cols, flags, seed & (2**64 - 1), _ptr(amax), o["alpha"].data_ptr(),
+        o["codes"].data_ptr(), o["scales"].data_ptr(), _ptr(o.get("choice")),
+        _ptr(o.get("codes_t")), _ptr(o.get("scales_t")), _stream(stream)))
     return o
 
 

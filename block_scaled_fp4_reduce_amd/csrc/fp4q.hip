@@ -2,6 +2,9 @@
 // launches on the caller's stream.  See include/fp4q.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/fp4q.h"
 #include "msed_kernels.h"
 #include "mxgemm_kernels.h"
@@ -12,6 +15,14 @@
 #include "rows_kernels.h"
 
 using namespace fp4q;
+
+// Workspace of nvfp4_quantize_noalloc: the amax pass's per-workgroup partial
+// maxima, in a fixed device array instead of caller memory.  Each device
+// holds its own copy (at its own address) until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device memory: the
+// device address comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kScratchBytes = 4096;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
 
 namespace {
 
@@ -92,6 +103,28 @@ hipError_t launch_1d(const uint16_t* x, int64_t nblocks, const uint32_t* abits, 
   return launch(nvfp4_1d_kernel<F46, SR, RHT>, (unsigned)grid, kThreads, st, (const uint4*)x,
                 nblocks, abits, namax, alpha_out, (uint2*)codes, scales, choice, (uint32_t)seed,
                 (uint32_t)(seed >> 32));
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP4_E_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP4_E_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP4_OK;
 }
 
 template <bool F46, bool SR, bool RHT>
@@ -230,7 +263,8 @@ int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flag
 
 namespace {
 
-// Argument checks of nvfp4_quantize.
+// Argument checks of nvfp4_quantize (and its no-allocation variant, with
+// the library's array as ws).
 int check_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
                          const float* amax_in, const float* alpha_out, const uint8_t* codes,
                          const uint8_t* scales, const uint8_t* codes_t, const uint8_t* scales_t,
@@ -302,6 +336,25 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   else e = first(e, FP4Q_1D(false, false, false));
 #undef FP4Q_1D
   return launched(e);
+}
+
+int nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags,
+                           uint64_t seed, const float* amax_in, float* alpha_out, uint8_t* codes,
+                           uint8_t* scales, uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
+                           void* stream) {
+  static_assert(kAmaxMaxGroups * sizeof(uint32_t) <= kScratchBytes, "amax partials fit");
+  if (amax_in)                           // no amax pass: no workspace at all
+    return nvfp4_quantize(x, rows, cols, flags, seed, amax_in, alpha_out, codes, scales, choice,
+                          codes_t, scales_t, nullptr, 0, stream);
+  // every argument check first (the array stands in for ws), then the
+  // array's device address
+  if (int rc = check_nvfp4_quantize(x, rows, cols, flags, amax_in, alpha_out, codes, scales,
+                                    codes_t, scales_t, &g_scratch, kScratchBytes))
+    return rc;
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  return nvfp4_quantize(x, rows, cols, flags, seed, nullptr, alpha_out, codes, scales, choice,
+                        codes_t, scales_t, ws, kScratchBytes, stream);
 }
 
 int nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, const float* alpha,

@@ -21,7 +21,8 @@
  * Conventions shared by every call:
  *  - Every tensor pointer is a DEVICE pointer (HIP device memory of the
  *    current device).  The caller allocates every buffer and owns it; the
- *    library allocates nothing and keeps no state between calls.
+ *    library allocates nothing and keeps no state between calls (except the
+ *    fixed per-device array of nvfp4_quantize_noalloc).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is queued on it asynchronously; the call returns before the GPU
  *    finishes.  Concurrent calls on different streams are safe as long as
@@ -130,6 +131,26 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                    float* alpha_out, uint8_t* codes, uint8_t* scales,
                    uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* nvfp4_quantize for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call without a workspace argument.  With amax_in ==
+ * NULL the amax pass keeps its per-workgroup partial maxima in a fixed
+ * 4 KiB device array of the library (one per device, held until the process
+ * ends; its address is looked up once per device on the first call there)
+ * instead of caller memory.  The call allocates nothing.
+ *   Arguments, results and errors as nvfp4_quantize; FP4_E_WORKSPACE if the
+ *   shape and flags would need more than that array (never for the flag
+ *   sets nvfp4_quantize accepts).
+ *   Every call on one device shares that array: calls that overlap in time
+ *   on one device (different streams, or host threads) race and may produce
+ *   wrong results; calls in one stream's order are safe.  Nothing in it
+ *   needs to start at zero (each call writes every partial it reads). */
+int nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols,
+                           uint32_t flags, uint64_t seed, const float* amax_in,
+                           float* alpha_out, uint8_t* codes, uint8_t* scales,
+                           uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
+                           void* stream);
 
 /* NVFP4 with one FP32 scale per row, quantized in a single read of x.  The
  * NVIDIA NVFP4 article (sec. 9) names the extra memory pass for the global

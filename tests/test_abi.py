@@ -172,3 +172,14 @@ def test_empty_tensors_need_no_buffers(L):
     assert L.mxfp4_quantize(None, 0, 64, fp4.ROWWISE, None, None, None, None, None) == OK
     assert L.fp4_dequantize(1, None, None, None, 0, 64, 0, None, None) == OK
 
+
+def test_noalloc_rejects_before_any_hip_call(L):
+    def nq(x=P, rows=32, cols=64, flags=0, amax=None, alpha=F4, codes=P, scales=P):
+        return L.nvfp4_quantize_noalloc(x, rows, cols, flags, 0, amax, alpha, codes, scales, None,
+                                        None, None, None)
+    assert nq(x=None) == E_NULL
+    assert nq(alpha=None) == E_NULL
+    assert nq(cols=40) == E_SHAPE
+    assert nq(flags=fp4.SR | fp4.FOUR_OVER_SIX) == E_FLAGS
+    assert nq(codes=Q) == E_ALIGN
+    assert nq(amax=F4, x=None) == E_NULL          # with an amax it is nvfp4_quantize's check
