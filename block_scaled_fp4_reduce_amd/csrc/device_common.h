@@ -247,13 +247,20 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
 
-// Max over the 16 lanes of a DPP row, in every lane of the row (the xor-1,
-// xor-2, half-mirror and mirror steps pair the lanes as a butterfly would).
+// Max of a non-negative value over the 16 lanes of a DPP row, in every lane
+// of the row (the xor-1, xor-2, half-mirror and mirror steps pair the lanes
+// as a butterfly would).  Non-negative floats order like their bit
+// patterns, so this is an integer max (one DPP max instruction per step).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
 __device__ __forceinline__ float tile_max(float v) {
-  v = fmaxf(v, dpp_f<kDppXor1>(v));
-  v = fmaxf(v, dpp_f<kDppXor2>(v));
-  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  return fmaxf(v, dpp_f<kDppMirror>(v));
+  uint32_t u = __float_as_uint(v);
+  u = max(u, dpp_row_u<kDppXor1>(u));
+  u = max(u, dpp_row_u<kDppXor2>(u));
+  u = max(u, dpp_row_u<kDppHalfMirror>(u));
+  return __uint_as_float(max(u, dpp_row_u<kDppMirror>(u)));
 }
 
 // Max of a non-negative value over the whole (fully active) wave, as a

@@ -12,9 +12,9 @@
 // The tile maximum and the 4/6 error sum are xor-butterflies over the 16
 // lanes (offsets 1, 2, 4, 8), i.e. a pairwise tree over the 16 row errors
 // whose result is bit-identical in every lane.  The transposed codes are
-// recomputed from an LDS copy of the tile with the same scale, so they are
-// the same fp32 operations on the same values and equal the row-wise codes
-// by construction.  The codes of a workgroup tile (64 x 256 values) are
+// the row-wise codes transposed inside the tile's 16 lanes (DPP exchanges
+// and byte/nibble merges): a tile has one scale, so the transpose's code of
+// an element is its row-wise code.  The codes of a workgroup tile (64 x 256 values) are
 // staged in LDS and leave in 16-byte runs: 128 bytes per row row-wise, 32
 // bytes per row of the transposed codes (a store that scatters 8-byte
 // pieces over 64 lines costs far more).  Workgroups are persistent (the
@@ -33,7 +33,6 @@ namespace fp4q {
 constexpr bool kHave2D = true;
 constexpr int k2dStrips = 4;                 // 64-column strips per workgroup
 constexpr int k2dSuperY = 16, k2dSuperX = 4; // workgroups per XCD super-tile (1024x1024 values)
-constexpr int k2dTileLds = 16 * 16 + 16;     // bf16 per tile in LDS (+32 B pad: no bank conflicts)
 // Code staging per workgroup tile (64 rows x 256 columns), two buffers:
 // row-wise codes 64 rows x 128 B, transposed codes 256 rows x 32 B (pitches
 // padded against bank conflicts).
@@ -61,6 +60,48 @@ __device__ __forceinline__ float tile_sum(float v) {
   return v + dpp_f<kDppMirror>(v);
 }
 
+constexpr int kDppRor8 = 0x128;           // lane i <- lane (i + 8) % 16 = i ^ 8
+constexpr int kDppQuadReverse = 0x1B;     // quad_perm [3,2,1,0]
+
+// Per-lane constants of transpose16 (lane r of its 16-lane row).
+struct NibbleT {
+  uint32_t sel4, sel2, mask1, rot1;
+  __device__ __forceinline__ explicit NibbleT(int r)
+      : sel4((r & 4) ? 0x03020706u : 0x05040100u),
+        sel2((r & 2) ? 0x03070105u : 0x06020400u),
+        mask1((r & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu),
+        rot1((r & 1) ? 4u : 28u) {}
+};
+
+// One 8x8 nibble matrix per 8-lane group (lane i: row i, element j in
+// nibble j) -> its transpose (lane i: column i), by exchanging 4x4, 2x2 and
+// 1x1 blocks with lane i ^ 4, i ^ 2, i ^ 1.
+__device__ __forceinline__ uint32_t transpose8_nibbles(uint32_t v, const NibbleT& k) {
+  // i ^ 4 inside each 8 lanes: half-row mirror (i -> 7 - i), then quad reverse
+  uint32_t p = dpp_row_u<kDppQuadReverse>(dpp_row_u<kDppHalfMirror>(v));
+  v = __builtin_amdgcn_perm(p, v, k.sel4);    // 16-bit halves: keep own, take partner's
+  p = dpp_row_u<kDppXor2>(v);
+  v = __builtin_amdgcn_perm(p, v, k.sel2);    // bytes
+  p = dpp_row_u<kDppXor1>(v);
+  p = __builtin_amdgcn_alignbit(p, p, k.rot1);
+  return (k.mask1 & v) | (~k.mask1 & p);      // nibbles (one v_bfi_b32)
+}
+
+// Transpose of a 16x16 tile's 4-bit codes held one row per lane of a
+// 16-lane DPP row (lane r: w0 = elements (r, 0..7), w1 = (r, 8..15), element
+// j in nibble j): lane c gets column c, t0 = elements (0..7, c), t1 =
+// (8..15, c).  The 8x8 blocks are exchanged with lane r ^ 8, then each 8x8
+// block is transposed inside its 8 lanes.  A tile's transposed codes are its
+// codes transposed (same values, same scale), so this is exact.
+__device__ __forceinline__ void transpose16_nibbles(uint32_t w0, uint32_t w1, int r,
+                                                    const NibbleT& k, uint32_t& t0,
+                                                    uint32_t& t1) {
+  const uint32_t p0 = dpp_row_u<kDppRor8>(w0), p1 = dpp_row_u<kDppRor8>(w1);
+  const bool hi = (r & 8) != 0;
+  t0 = transpose8_nibbles(hi ? p1 : w0, k);    // rows 0..7 of this lane's 8 columns
+  t1 = transpose8_nibbles(hi ? w1 : p0, k);    // rows 8..15
+}
+
 template <bool FOUR_SIX, bool TRANSPOSE>
 __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
@@ -69,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
   __shared__ float2 tab[128];
   __shared__ uint32_t red[kThreads / 64];
-  __shared__ uint16_t stage[kThreads / 64][4][k2dTileLds];
   __shared__ __align__(16) uint8_t cst_r[2][64 * k2dRowPitch];
   __shared__ __align__(16) uint8_t cst_t[2][TRANSPOSE ? 256 * k2dColPitch : 8];
 
@@ -92,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
   __syncthreads();
   if (nslots == 0) return;                   // empty tensor: only the tensor scale
 
-  uint16_t* st = stage[wave][tile];
+  const NibbleT nt(r);
   // Decode `slot` and load this lane's row of its 4 strips.  Every load is
   // issued (addresses clamped into the tensor) so the compiler keeps the
   // next workgroup tile's loads in flight while this one is computed;
@@ -135,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
 
       uint32_t e6, e4;
       e4m3_pair(amax_b * ts.k6, amax_b * ts.k4, e6, e4);
-      float2 sr = tab[e6];
+      const float2 sr = tab[e6];
       uint32_t w0, w1, scale = e6, pick4 = 0;
       const float err6 = tile_sum(quant16_rtn(y, sr.x, sr.y, w0, w1));
       if constexpr (FOUR_SIX) {
@@ -143,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
         uint32_t u0, u1;
         const float err4 = tile_sum(quant16_rtn(y, sr4.x, sr4.y, u0, u1));
         if (err4 < err6) {  // ties keep M = 6; identical in all 16 lanes
-          w0 = u0; w1 = u1; scale = e4; pick4 = 1; sr = sr4;
+          w0 = u0; w1 = u1; scale = e4; pick4 = 1;
         }
       }
       *(uint2*)(cs_row + (wave * 16 + r) * k2dRowPitch + (s * 4 + tile) * 8) = make_uint2(w0, w1);
@@ -154,28 +194,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_2d_kernel(
         }
       }
       if constexpr (TRANSPOSE) {
-        // stage the tile (bf16, row r at st[16 r]), then lane r takes column r;
-        // each wave uses its own LDS slots, so a wave-level sync suffices
-        *(uint4*)(st + 16 * r) = v0;
-        *(uint4*)(st + 16 * r + 8) = v1;
-        wave_lds_sync();
-        float yc[16];
-#pragma unroll
-        for (int k = 0; k < 16; k++) yc[k] = __uint_as_float((uint32_t)st[16 * k + r] << 16);
-        const float rr = sr.y;
-        uint32_t t0 = 0, t1 = 0;
-        t0 = cvt_fp4x2<0>(t0, yc[0] * rr, yc[1] * rr, 1.0f);
-        t0 = cvt_fp4x2<1>(t0, yc[2] * rr, yc[3] * rr, 1.0f);
-        t0 = cvt_fp4x2<2>(t0, yc[4] * rr, yc[5] * rr, 1.0f);
-        t0 = cvt_fp4x2<3>(t0, yc[6] * rr, yc[7] * rr, 1.0f);
-        t1 = cvt_fp4x2<0>(t1, yc[8] * rr, yc[9] * rr, 1.0f);
-        t1 = cvt_fp4x2<1>(t1, yc[10] * rr, yc[11] * rr, 1.0f);
-        t1 = cvt_fp4x2<2>(t1, yc[12] * rr, yc[13] * rr, 1.0f);
-        t1 = cvt_fp4x2<3>(t1, yc[14] * rr, yc[15] * rr, 1.0f);
-        // column 16*tile + r of the strip, tile row `wave`: 8 bytes
+        // the tile's column r of codes: the row codes transposed across the
+        // tile's 16 lanes (column 16*tile + r of the strip, tile row `wave`)
+        uint32_t t0, t1;
+        transpose16_nibbles(w0, w1, r, nt, t0, t1);
         *(uint2*)(cs_col + ((s * 4 + tile) * 16 + r) * k2dColPitch + wave * 8) = make_uint2(t0, t1);
         if (ok && r == 0) scales_t[bc * brows + br] = (uint8_t)scale;
-        wave_lds_sync();                   // reads done before the next strip's writes
       }
     }
     // Every wave's codes of this workgroup tile are staged: write them out
