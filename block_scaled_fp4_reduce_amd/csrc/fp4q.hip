@@ -439,7 +439,7 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
                const uint8_t* bt_scales, int64_t M, int64_t N, int64_t K, float* c,
                void* stream) {
   if (M < 0 || N < 0 || K < 0) return FP4_E_SHAPE;
-  if (K % kGemmBK) return FP4_E_SHAPE;
+  if (K % kGemmKMultiple) return FP4_E_SHAPE;
   if ((M > 0 && K > 0 && (!a_codes || !a_scales)) || (N > 0 && K > 0 && (!bt_codes || !bt_scales)) ||
       (M > 0 && N > 0 && !c))
     return FP4_E_NULL;
