@@ -174,6 +174,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;   // LDS destination of direct loads
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 // Cache policy of quantizer output stores: non-temporal (streaming), for

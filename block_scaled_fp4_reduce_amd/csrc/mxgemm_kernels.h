@@ -52,7 +52,6 @@ constexpr int kCachePolicyNt = 2;                  // buffer-op cache policy: no
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // One LDS stage: both operands' codes and scale dwords.
 struct GemmStageLds {
@@ -214,12 +213,9 @@ __device__ __forceinline__ void gemm_mfma_step(f32x16_t (&acc)[kGemmMI][kGemmNJ]
   }
 }
 
-// Instruction order hints for the scheduler (masks: 0x008 matrix, 0x020
-// vector-memory read, 0x100 LDS read).  Three steps of the stage: each
-// matrix instruction of the first half of a step is followed by one LDS read
-// of the next step's operands.  The last step: its matrix instructions
-// interleaved with the 20 direct loads of the stage after next and the 12
-// reads of the next stage's scales and first operands.
+// Instruction order hints for the scheduler (masks: 0x008 matrix, 0x100
+// LDS read) for steps 0..2 of a stage: each matrix instruction of the first
+// half of a step is followed by one LDS read of the next step's operands.
 __device__ __forceinline__ void gemm_order_steps012() {
 #pragma unroll
   for (int st = 0; st < 3; st++) {
@@ -231,19 +227,6 @@ __device__ __forceinline__ void gemm_order_steps012() {
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
 }
-__device__ __forceinline__ void gemm_order_step3() {
-#pragma unroll
-  for (int k = 0; k < 12; k++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x010, 5, 0);
-  }
-}
-
 __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ bt_codes, const uint8_t* __restrict__ bt_scales, int64_t M,
@@ -281,7 +264,8 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
   //   wait until this wave's LDS reads are done and its loads of stage
   //     ks + 1 have landed, then the barrier: ring[(ks + 1) % 2] is whole
   //     and nobody reads ring[ks % 2] any more;
-  //   issue the loads of stage ks + 2 into ring[ks % 2];
+  //   issue the loads of stage ks + 2 into ring[ks % 2] (first: they get
+  //     the most time, and the TA works through them during step 3);
   //   step 3, with the reads of stage ks + 1's scales and step-0 operands.
   // The loads of a stage have four steps (64 instructions) to arrive.
   gemm_issue_stage(ring[0], q, ra, rb, rsa, rsb, rowb, srow, 0);
@@ -304,11 +288,10 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     gemm_order_steps012();
     wait_vmcnt<0, true>();
     gemm_barrier();
+    gemm_issue_stage(cur, q, ra, rb, rsa, rsb, rowb, srow, ks + 2);
     gemm_read_scales(nxt, nsc);
     gemm_read_ops(nxt, 0, o0);
-    gemm_issue_stage(cur, q, ra, rb, rsa, rsb, rowb, srow, ks + 2);
     gemm_mfma_step(acc, o1, sc, 3);
-    gemm_order_step3();
     sc = nsc;
   };
   for (int ks = 0; ks < nk; ks += 2) {
