@@ -14,14 +14,15 @@ Reported on one JSON line:
   * value / ms_per_step: effective GB/s of the whole step over the
     algorithmic bytes (bf16 read + FP4 codes + E4M3 scales + 4 B tensor
     scale), timed over exactly --steps steps with HIP events;
-  * the quantize kernel alone (amax given), over >= 100 launches: the mean
+  * the quantize kernel alone (amax given), over >= 250 launches: the mean
     of back-to-back launches (events around the whole run) and the median,
-    p10 and p90 over batches of 10 back-to-back launches (per-launch
+    p10 and p90 over batches of 25 back-to-back launches (per-launch
     durations of single kernels are in the rocprofv3 kernel-trace summary);
   * the roofline of that kernel: HBM (algorithmic bytes / mean launch time
-    against 8 TB/s) and vector-ALU issue (issue slots per launch from the
-    committed rocprofv3 counter summary, against 614.4 G wave64 issue slots
-    per second: 256 CUs x 4 SIMDs x 2.4 GHz / 4 cycles); `bound` names the
+    against 8 TB/s) and vector-ALU issue (SQ_ACTIVE_INST_VALU per launch
+    from the committed rocprofv3 counter summary: one per wave64 VALU
+    instruction, two for the 8-cycle conversions, against 1228.8 G per second:
+    256 CUs x 4 SIMDs x 2.4 GHz / 2 cycles); `bound` names the
     larger fraction.  Traffic (FETCH_SIZE + WRITE_SIZE, calibrated) and the
     issue slots come from that summary only while the kernel sources it was
     taken on are unchanged, else null;
@@ -46,12 +47,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# wave64 VALU issue slots per second: 256 CUs x 4 SIMDs, one wave64
-# instruction per SIMD every 4 cycles at 2.4 GHz (= 78.6 TFLOP/s of
-# non-packed fp32 FMA; packed fp32 is not used)
-VALU_PEAK_GSLOTS = 256 * 4 * 2.4 / 4
+# wave64 VALU instructions per second: 256 CUs x 4 SIMDs, one wave64 fp32
+# FMA per SIMD every 2 cycles at 2.4 GHz -- the rate behind the published
+# 157.3 TFLOP/s fp32 vector peak (a non-packed v_fma_f32 measures 2.3-2.4
+# cycles per wave64 instruction on gfx950; instructions with an SGPR operand,
+# max3/med3, shifts and bit ops about 4.3, the fp4/fp8 conversions 8.4, so a
+# real mix tops out well below this)
+VALU_PEAK_GSLOTS = 256 * 4 * 2.4 / 2
 MFMA_FP4_PEAK_TFLOPS = 10100.0                  # dense FP4 matrix peak of MI355X
-MIN_LAUNCHES = 100                               # kernel-only figures: launches timed
+MIN_LAUNCHES = 250                               # kernel-only figures: launches timed
 # the kernel that does each workload's quantization (amax given)
 KERNEL_OF = {"c1": "nvfp4_1d_kernel<false, false, false>",
              "c2": "nvfp4_1d_kernel<true, false, false>",
@@ -159,8 +163,15 @@ def roofline(wl, us):
     if slots:
         ach = slots / us / 1e3                        # G slots per second
         out["valu"] = {"achieved": round(ach, 1), "peak": VALU_PEAK_GSLOTS,
-                       "unit": "G wave64 VALU issue slots/s", "frac": round(ach / VALU_PEAK_GSLOTS, 4),
+                       "unit": "G wave64 VALU issues/s", "frac": round(ach / VALU_PEAK_GSLOTS, 4),
                        "issue_slots_per_launch": slots, "valu_insts_per_launch": c.get("valu_insts")}
+        if c.get("clock_ghz"):                        # the same issue slots at the measured clock
+            peak_at = 256 * 4 * c["clock_ghz"] / 4
+            out["valu"].update(clock_ghz=c["clock_ghz"], peak_at_clock=round(peak_at, 1),
+                               frac_at_clock=round(ach / peak_at, 4))
+    if c.get("mfma_busy_frac") is not None:
+        out["mfma_busy_frac"] = c["mfma_busy_frac"]
+        out["clock_ghz"] = c.get("clock_ghz")
     return out
 
 
@@ -311,14 +322,25 @@ class Row:
         assert rc == 0, rc
 
 
+def head_start(torch, calls):
+    """Keep the GPU busy (a spin kernel on the current stream) while the host
+    enqueues `calls` launches: a ctypes call plus a launch costs the host
+    about as long as the shortest kernels run, so without a head start the
+    queue would drain between launches and the timing would measure the
+    host.  The spin ends before the first timing event."""
+    torch.cuda._sleep(int(max(2e-3, calls * 30e-6) * 2.4e9))
+
+
 def time_loop(torch, stream, fn, steps, warmup):
     """Mean ms per call of `steps` back-to-back calls (HIP events on the
-    launch stream around the whole run) and the host wall time."""
+    launch stream around the whole run, the calls queued behind a head
+    start) and the host wall time."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    head_start(torch, steps)
     e0.record(stream)
     for i in range(steps):
         fn(i)
@@ -328,16 +350,17 @@ def time_loop(torch, stream, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def launch_stats(torch, stream, fn, n, warmup, batch=10):
+def launch_stats(torch, stream, fn, n, warmup, batch=25):
     """n calls: the mean of back-to-back calls (HIP events around the whole
     run; it includes the short dispatch gap between consecutive kernels,
     which rocprofv3's kernel duration excludes) and the median, p10 and p90
     over n / batch batches of `batch` back-to-back calls (an event pair per
-    batch: an event recorded between every two calls would add several us
-    to each), as us per call."""
+    batch: each event costs about 5 us of pipeline drain, so batches of 25
+    keep the median within 1 % of the back-to-back mean), as us per call."""
     mean_ms, _ = time_loop(torch, stream, fn, n, warmup)
     nb = max(1, n // batch)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    head_start(torch, n)
     ev[0].record(stream)
     for b in range(nb):
         for i in range(batch):
@@ -605,10 +628,24 @@ def summarize(out_path, dirs, command):
                 e["hbm_bytes"] = e["fetch_bytes"] + e["write_bytes"]
             if "SQ_INSTS_VALU" in q:
                 e["valu_insts"] = round(q["SQ_INSTS_VALU"])
-            if "SQ_ACTIVE_INST_VALU" in q:            # units of 4 cycles of one SIMD
+            if "SQ_ACTIVE_INST_VALU" in q:            # wave64 VALU issues (8-cycle ones count 2)
                 e["valu_issue_slots"] = round(q["SQ_ACTIVE_INST_VALU"])
             if kern in durations:
                 e["avg_us_trace"] = round(sum(durations[kern]) / len(durations[kern]), 3)
+            # shader clock over the kernel: GRBM_GUI_ACTIVE counts busy cycles
+            # on each of the 8 XCDs over the profiled dispatch, which adds a
+            # few us of launch and drain to the kernel's duration, so the
+            # figure is kept for kernels of 150 us and more only (there the
+            # excess is under 2 %)
+            if "GRBM_GUI_ACTIVE" in q and kern in durations:
+                us = statistics.median(durations[kern])
+                if us >= 150.0:
+                    e["clock_ghz"] = round(q["GRBM_GUI_ACTIVE"] / 8 / (us * 1e3), 3)
+            # matrix-core busy cycles (summed over SIMDs) over the CU busy
+            # cycles of 4 SIMDs each
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in q and q.get("SQ_BUSY_CU_CYCLES"):
+                e["mfma_busy_frac"] = round(q["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                            (4 * q["SQ_BUSY_CU_CYCLES"]), 4)
             merged[wl] = e
             alg = algorithmic_bytes(wl)
             lines.append("| %s | %s | %s | %s | %s | %s | %s |" % (
@@ -647,7 +684,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this quantizer has no multi-GPU path "
-              "(sharding needs one all-reduce(max) of the amax; see DESIGN.md)", file=sys.stderr)
+              "(sharding needs one all-reduce(max) of the amax)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -735,10 +772,14 @@ def main():
             if r.kind == "gemm":
                 fl = 2.0 * r.rows * GEMM_N * r.cols
                 tf = fl / ks["us_mean"] / 1e6
+                rw = roofline(wl, ks["us_mean"])
                 entry = {"workload": r.label, "flops": fl, "kernel": ks,
                          "tflops": round(tf, 1), "kernel_frac_mfma_fp4": round(tf / MFMA_FP4_PEAK_TFLOPS, 4),
-                         "bound": "mfma", "hbm": roofline(wl, ks["us_mean"])["hbm"],
-                         "traffic": roofline(wl, ks["us_mean"])["traffic"]}
+                         "bound": "mfma", "hbm": rw["hbm"], "traffic": rw["traffic"],
+                         "mfma_busy_frac": rw.get("mfma_busy_frac"), "clock_ghz": rw.get("clock_ghz")}
+                if rw.get("clock_ghz"):               # the FP4 peak at the measured clock
+                    entry["kernel_frac_mfma_fp4_at_clock"] = round(
+                        tf / (MFMA_FP4_PEAK_TFLOPS * rw["clock_ghz"] / 2.4), 4)
             else:
                 a = algorithmic_bytes(wl)
                 rw = roofline(wl, ks["us_mean"])
