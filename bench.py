@@ -86,6 +86,10 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_by_workload.json")
 ROWS = {
     "c1": (256, 1024, "nvfp4", 0, "nvfp4_rtn6_256x1024"),
     "c2": (8192, 4096, "nvfp4", 1, "nvfp4_four_over_six_8192x4096"),
+    # not a bench row: c2's tensor and bytes with plain RTN6 (no 4/6
+    # candidates, about half the vector work), the reference that shows
+    # what the traffic alone costs
+    "c2r": (8192, 4096, "nvfp4", 0, "nvfp4_rtn6_8192x4096_same_traffic"),
     "c3": (14336, 4096, "nvfp4", 1 | 8 | 64, "nvfp4_2d16x16_four_over_six_transposed_14336x4096"),
     "c4": (8192, 14336, "nvfp4", 2 | 4, "nvfp4_rht16_sr_8192x14336"),
     "c5": (16384, 8192, "mxfp4", 16 | 32 | 64, "mxfp4_had32_row_col_16384x8192"),
@@ -102,7 +106,7 @@ ROWS = {
     "f4g": (8192, 14336, "requant", 2 | 4, "nvfp4_requant_t_rht16_sr_8192x14336"),
 }
 # workload -> the seeded tensor it quantizes, where that is another workload's
-DATA_OF = {"f1": "c4", "f2": "c2", "f3": "c5"}
+DATA_OF = {"f1": "c4", "f2": "c2", "f3": "c5", "c2r": "c2"}
 GEMM_N = 8192                                   # f3: B^T rows (N); K = the tensor's cols
 # requant workload -> (workload whose quantization is the input, its flags)
 REQUANT_SRC = {"f4a": ("c2", 1), "f4g": ("c4", 2 | 4)}
@@ -325,9 +329,9 @@ class Row:
 def head_start(torch, calls):
     """Keep the GPU busy (a spin kernel on the current stream) while the host
     enqueues `calls` launches: a ctypes call plus a launch costs the host
-    about as long as the shortest kernels run, so without a head start the
-    queue would drain between launches and the timing would measure the
-    host.  The spin ends before the first timing event."""
+    about 4 us, longer than the shortest kernels (c1: 3 us) run, so without
+    a head start the queue would drain between launches and the timing
+    would measure the host.  The spin ends before the first timing event."""
     torch.cuda._sleep(int(max(2e-3, calls * 30e-6) * 2.4e9))
 
 
@@ -721,6 +725,10 @@ def main():
     kst = launch_stats(torch, head.stream, head.kernel, args.launches, args.warmup)
     sst = launch_stats(torch, head.stream, head.step, args.launches, args.warmup)
     copy_gbs = copy_reference(torch, head)
+    ref = Row("c2r", fp4, torch, synthetic, np)
+    rst = launch_stats(torch, ref.stream, ref.kernel, args.launches, args.warmup)
+    del ref
+    torch.cuda.empty_cache()
     alg = algorithmic_bytes("c2")
     value = alg / (ms_step * 1e-3) / 1e9
     rl = roofline("c2", kst["us_mean"])
@@ -755,6 +763,8 @@ def main():
         "target_70pct_of_hbm": {"A_quantize_kernel_mean": rl["hbm"]["frac"] >= 0.7,
                                 "B_full_step": value / HBM_PEAK_GBS >= 0.7},
         "copy_kernel_gbs": round(copy_gbs, 1),
+        "same_traffic_rtn6_kernel": dict(rst, note="the same tensor and bytes quantized with plain "
+                                         "RTN6: no 4/6 candidates, about half the vector work"),
         "roofline": {"bound": "alu" if bound == "alu" else "hbm",
                      "achieved": main_roof["achieved"], "peak": main_roof["peak"],
                      "unit": main_roof["unit"], "frac": main_roof["frac"],
