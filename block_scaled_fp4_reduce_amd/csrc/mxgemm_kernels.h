@@ -163,6 +163,13 @@ struct GemmOps {
 struct GemmScales {
   u32x4_t a[2], b[2];
 };
+// The same scales as the instruction takes them: for each of the 4 A and 4
+// B rows one word holding the bytes of this lane's K half, byte `sub` for
+// step sub (bytes 0, 2, 4, 6 of the row's 8 for lanes 0..31, bytes 1, 3, 5,
+// 7 for lanes 32..63), so the instruction's byte select picks it.
+struct GemmScaleWords {
+  uint32_t a[kGemmMI], b[kGemmNJ];
+};
 
 // Read the operands of step `sub` (K values 64 sub .. 64 sub + 63 of the
 // stage): lane (r, g) takes chunk 2 sub + g of its rows.
@@ -187,16 +194,22 @@ __device__ __forceinline__ void gemm_read_scales(const GemmStageLds& st, GemmSca
   s.b[1] = *(const u32x4_t*)(st.sb + 256 * wn + 128 + 4 * r);
 }
 
-// The 16 matrix instructions of step `sub`.
+__device__ __forceinline__ void gemm_scale_words(const GemmScales& s, GemmScaleWords& w) {
+  // v_perm_b32 byte selects over (hi = bytes 4..7, lo = bytes 0..3)
+  const uint32_t sel = (threadIdx.x & 32) ? 0x07050301u : 0x06040200u;
+#pragma unroll
+  for (int i = 0; i < kGemmMI; i++)
+    w.a[i] = __builtin_amdgcn_perm(s.a[i >> 1][2 * (i & 1) + 1], s.a[i >> 1][2 * (i & 1)], sel);
+#pragma unroll
+  for (int j = 0; j < kGemmNJ; j++)
+    w.b[j] = __builtin_amdgcn_perm(s.b[j >> 1][2 * (j & 1) + 1], s.b[j >> 1][2 * (j & 1)], sel);
+}
+
+// The 16 matrix instructions of step SUB; the scale byte is selected by
+// the instruction (op_sel), from the words of gemm_scale_words.
+template <int SUB>
 __device__ __forceinline__ void gemm_mfma_step(f32x16_t (&acc)[kGemmMI][kGemmNJ],
-                                               const GemmOps& o, const GemmScales& s, int sub) {
-  // byte 2 sub + g of the row's 8: dword sub / 2, byte 2 (sub % 2) + g
-  const int d = sub >> 1, shift = 8 * (2 * (sub & 1) + ((threadIdx.x & 63) >> 5));
-  int ea[kGemmMI], eb[kGemmNJ];
-#pragma unroll
-  for (int i = 0; i < kGemmMI; i++) ea[i] = (int)((s.a[i >> 1][2 * (i & 1) + d] >> shift) & 0xFFu);
-#pragma unroll
-  for (int j = 0; j < kGemmNJ; j++) eb[j] = (int)((s.b[j >> 1][2 * (j & 1) + d] >> shift) & 0xFFu);
+                                               const GemmOps& o, const GemmScaleWords& w) {
   // FP4 operands fill the low four registers of the instruction's eight; the
   // upper four are not read (left undefined rather than zeroed)
 #pragma unroll
@@ -207,8 +220,8 @@ __device__ __forceinline__ void gemm_mfma_step(f32x16_t (&acc)[kGemmMI][kGemmNJ]
     for (int j = 0; j < kGemmNJ; j++) {
       const i32x8_t bv = __builtin_shufflevector((i32x4_t)o.b[j], (i32x4_t)o.b[j], 0, 1, 2, 3, -1,
                                                  -1, -1, -1);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 4, 4, 0, ea[i],
-                                                                  0, eb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          av, bv, acc[i][j], 4, 4, SUB, (int)w.a[i], SUB, (int)w.b[j]);
     }
   }
 }
@@ -273,25 +286,28 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
   wait_vmcnt<kGemmLoadsPerStage, false>();
   gemm_barrier();
   GemmOps o0, o1;
-  GemmScales sc, nsc;
-  gemm_read_scales(ring[0], sc);
+  GemmScales rs;
+  GemmScaleWords sc, nsc;
+  gemm_read_scales(ring[0], rs);
+  gemm_scale_words(rs, sc);
   gemm_read_ops(ring[0], 0, o0);
   // the two buffers alternate by name (unrolled by two), so that the
   // compiler sees which one each LDS read and direct load touches
   auto stage = [&](GemmStageLds& cur, GemmStageLds& nxt, int ks) {
     gemm_read_ops(cur, 1, o1);
-    gemm_mfma_step(acc, o0, sc, 0);
+    gemm_mfma_step<0>(acc, o0, sc);
     gemm_read_ops(cur, 2, o0);
-    gemm_mfma_step(acc, o1, sc, 1);
+    gemm_mfma_step<1>(acc, o1, sc);
     gemm_read_ops(cur, 3, o1);
-    gemm_mfma_step(acc, o0, sc, 2);
+    gemm_mfma_step<2>(acc, o0, sc);
     gemm_order_steps012();
     wait_vmcnt<0, true>();
     gemm_barrier();
     gemm_issue_stage(cur, q, ra, rb, rsa, rsb, rowb, srow, ks + 2);
-    gemm_read_scales(nxt, nsc);
+    gemm_read_scales(nxt, rs);
     gemm_read_ops(nxt, 0, o0);
-    gemm_mfma_step(acc, o1, sc, 3);
+    gemm_scale_words(rs, nsc);
+    gemm_mfma_step<3>(acc, o1, sc);
     sc = nsc;
   };
   for (int ks = 0; ks < nk; ks += 2) {
