@@ -32,6 +32,7 @@ Reported on one JSON line:
     with the core count and CPU model.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-rows]
+                    [--rows c3,f3,...]
     python bench.py --summarize OUT.md DIR [DIR...]   # rocprofv3 output -> summary
 """
 from __future__ import annotations
@@ -676,6 +677,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timings")
     ap.add_argument("--no-rows", action="store_true", help="headline workload only")
+    ap.add_argument("--rows", default="", help="comma-separated subset of the other workloads "
+                    "(for profiling runs)")
     ap.add_argument("--launches", type=int, default=MIN_LAUNCHES,
                     help="launches per kernel-only figure (default %d; fewer only for "
                          "profiler runs)" % MIN_LAUNCHES)
@@ -696,6 +699,8 @@ def main():
     import synthetic as synthetic_mod
     synthetic = CachedGen(synthetic_mod)
     row_wls = () if args.no_rows else ("c1", "c3", "c4", "c5", "f1", "f2", "f3", "f4a", "f4g")
+    if args.rows:
+        row_wls = tuple(w for w in args.rows.split(",") if w in row_wls)
 
     # CPU oracle first, before this process touches the GPU (its all-core
     # run forks worker processes)
