@@ -264,6 +264,11 @@ class Row:
                 self.args_kernel.append(a)
         self.fn = {"nvfp4": L.nvfp4_quantize, "rows": L.nvfp4_quantize_rows,
                    "mxfp4": L.mxfp4_quantize}[kind]
+        # one call per buffer set before any timing: the first write to a
+        # freshly allocated output is slower (page mapping), and a short
+        # warm-up touches only some of the sets
+        for k in range(self.nbuf):
+            self.step(k)
         torch.cuda.synchronize()
 
     def _init_gemm(self, fp4, torch, synthetic, np, dev):
@@ -328,12 +333,15 @@ class Row:
 
 
 def head_start(torch, calls):
-    """Keep the GPU busy (a spin kernel on the current stream) while the host
-    enqueues `calls` launches: a ctypes call plus a launch costs the host
-    about 4 us, longer than the shortest kernels (c1: 3 us) run, so without
-    a head start the queue would drain between launches and the timing
-    would measure the host.  The spin ends before the first timing event."""
-    torch.cuda._sleep(int(max(2e-3, calls * 30e-6) * 2.4e9))
+    """Keep the GPU busy for 0.5 ms (a spin kernel on the current stream)
+    while the host starts enqueueing the timed launches: a ctypes call plus
+    a launch costs the host about 4 us, longer than the shortest kernels
+    (c1: 3 us) run.  The spin is kept short: after a longer one the chip's
+    clock has dropped and the next kernels run slower for milliseconds
+    (measured on the 4/6 kernel: 0.5 ms of spin 16.1 us per launch, 2 ms
+    17.2 us, 8 ms 18.1 us).  It ends before the first timing event."""
+    del calls
+    torch.cuda._sleep(int(0.5e-3 * 2.4e9))
 
 
 def time_loop(torch, stream, fn, steps, warmup):
