@@ -93,7 +93,7 @@ __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r << 2)) & 
 // the stage's 1 KiB piece j = 8 w + i: 16-byte position p = 64 j + lane is
 // row p / 8 = 64 w + 8 i + lane / 8, chunk (p % 8) ^ gemm_swz(row); the
 // permutation depends on row % 16 only, so load i is load i % 2 moved by
-// 8 (i - i % 2) rows (a uniform offset).  Scale dwords of a stage: row
+// 8 (i - i % 2) rows.  Scale dwords of a stage: row
 // 128 wm + 32 i + r, dword dw (bytes 4 dw .. 4 dw + 3 of its 8) at dword
 // 256 wm + 128 (i / 2) + 4 r + 2 (i % 2) + dw, so that a lane's four rows
 // are two 16-byte reads and 16 lanes read 256 consecutive bytes.  Scale
@@ -103,8 +103,10 @@ __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ (r << 2)) & 
 struct GemmSrc {
   uint32_t code[2];        // loads 0 and 1: row * rowb + 16 * chunk
   uint32_t code_k[2];      // 16 * chunk: byte of the stage within its row
+  uint32_t code_row[2];    // loads 0 and 1: the row (within the tile)
   uint32_t scale;          // load 0: row * srow + 4 * dw
   uint32_t scale_k;        // 4 * dw
+  uint32_t scale_row;      // load 0: the row
 };
 
 __device__ __forceinline__ void gemm_src(GemmSrc& q, int rowb, int srow) {
@@ -114,42 +116,48 @@ __device__ __forceinline__ void gemm_src(GemmSrc& q, int rowb, int srow) {
     const int row = 64 * wave + 8 * i + (lane >> 3), c = (lane & 7) ^ gemm_swz(row);
     q.code[i] = (uint32_t)(row * rowb + 16 * c);
     q.code_k[i] = (uint32_t)(16 * c);
+    q.code_row[i] = (uint32_t)row;
   }
   const int row = 128 * (wave >> 1) + 32 * (2 * (wave & 1) + ((lane >> 1) & 1)) + (lane >> 2);
   const int dw = lane & 1;
   q.scale = (uint32_t)(row * srow + 4 * dw);
   q.scale_k = (uint32_t)(4 * dw);
+  q.scale_row = (uint32_t)row;
 }
 
 // Issue the 20 direct loads of stage ks into `st` (8 + 8 code loads of 16
-// bytes, 2 + 2 scale loads of 4 bytes); bytes past K load as zeros (an
-// offset past the buffer stays past it with the row step added).
+// bytes, 2 + 2 scale loads of 4 bytes).  Bytes past K and rows past M (A)
+// or N (B) take an offset past the buffer, so they load as zeros; the
+// whole offset is per lane (the buffer's range check does not cover a
+// scalar offset).
 __device__ __forceinline__ void gemm_issue_stage(GemmStageLds& st, const GemmSrc& q,
                                                  __amdgpu_buffer_rsrc_t ra,
                                                  __amdgpu_buffer_rsrc_t rb,
                                                  __amdgpu_buffer_rsrc_t rsa,
                                                  __amdgpu_buffer_rsrc_t rsb, int rowb, int srow,
-                                                 int ks) {
+                                                 uint32_t mrows, uint32_t nrows, int ks) {
   // uniform: the LDS destinations are scalar (M0) addresses
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t kc = (uint32_t)(ks * kGemmRowBytes), kscale = (uint32_t)(ks * (kGemmBK / 32));
-  uint32_t off[2];
-#pragma unroll
-  for (int i = 0; i < 2; i++) off[i] = kc + q.code_k[i] < (uint32_t)rowb ? q.code[i] + kc : kGemmOob;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
+    const bool kin = kc + q.code_k[i & 1] < (uint32_t)rowb;
+    const uint32_t row = q.code_row[i & 1] + 8 * (i & ~1);
+    const uint32_t o = q.code[i & 1] + kc + (uint32_t)(8 * (i & ~1) * rowb);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(st.a + 1024 * (8 * wave + i)), 16,
-                                             off[i & 1], 8 * (i & ~1) * rowb, 0, 0);
+                                             kin && row < mrows ? o : kGemmOob, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(st.b + 1024 * (8 * wave + i)), 16,
-                                             off[i & 1], 8 * (i & ~1) * rowb, 0, 0);
+                                             kin && row < nrows ? o : kGemmOob, 0, 0, 0);
   }
-  const uint32_t soff = kscale + q.scale_k < (uint32_t)srow ? q.scale + kscale : kGemmOob;
+  const bool kin = kscale + q.scale_k < (uint32_t)srow;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
+    const uint32_t row = q.scale_row + 16 * i;
+    const uint32_t o = q.scale + kscale + (uint32_t)(16 * i * srow);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t*)(st.sa + 64 * (2 * wave + i)), 4,
-                                             soff, 16 * i * srow, 0, 0);
+                                             kin && row < mrows ? o : kGemmOob, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t*)(st.sb + 64 * (2 * wave + i)), 4,
-                                             soff, 16 * i * srow, 0, 0);
+                                             kin && row < nrows ? o : kGemmOob, 0, 0, 0);
   }
 }
 constexpr int kGemmLoadsPerStage = 20;
@@ -263,6 +271,7 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
       const_cast<uint8_t*>(bt_scales + n0 * srow), 0, (int)(nrows * srow), 0x00020000);
   GemmSrc q;
   gemm_src(q, rowb, srow);
+  const uint32_t mr = (uint32_t)mrows, nr = (uint32_t)nrows;
 
   f32x16_t acc[kGemmMI][kGemmNJ];
 #pragma unroll
@@ -281,8 +290,8 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
   //     the most time, and the TA works through them during step 3);
   //   step 3, with the reads of stage ks + 1's scales and step-0 operands.
   // The loads of a stage have four steps (64 instructions) to arrive.
-  gemm_issue_stage(ring[0], q, ra, rb, rsa, rsb, rowb, srow, 0);
-  gemm_issue_stage(ring[1], q, ra, rb, rsa, rsb, rowb, srow, 1);
+  gemm_issue_stage(ring[0], q, ra, rb, rsa, rsb, rowb, srow, mr, nr, 0);
+  gemm_issue_stage(ring[1], q, ra, rb, rsa, rsb, rowb, srow, mr, nr, 1);
   wait_vmcnt<kGemmLoadsPerStage, false>();
   gemm_barrier();
   GemmOps o0, o1;
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(kGemmThreads) void mxfp4_gemm_kernel(
     gemm_order_steps012();
     wait_vmcnt<0, true>();
     gemm_barrier();
-    gemm_issue_stage(cur, q, ra, rb, rsa, rsb, rowb, srow, ks + 2);
+    gemm_issue_stage(cur, q, ra, rb, rsa, rsb, rowb, srow, mr, nr, ks + 2);
     gemm_read_scales(nxt, rs);
     gemm_read_ops(nxt, 0, o0);
     gemm_scale_words(rs, nsc);
