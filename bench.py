@@ -134,6 +134,20 @@ def algorithmic_bytes(wl):
     return 2 * n + n // 2 + n // 16 + 4
 
 
+def expected_items(wl):
+    """Work-items of the workload's quantize launch, for the 1D quantizer
+    (whose kernel c1 shares with the same-traffic RTN6 reference row, so a
+    profile tells them apart by launch size only); None for other kernels.
+    Follows the 1D launch rule: one 256-thread workgroup per 256 blocks, at
+    most 6 (4 with SR) resident per CU of the 256."""
+    rows, cols, kind, flags, _ = ROWS[wl]
+    if kind != "nvfp4" or flags & (8 | 128):
+        return None
+    nblocks = rows * cols // 16
+    per_cu = 4 if flags & 2 else 6
+    return min(-(-nblocks // 256), 256 * per_cu) * 256
+
+
 def sources_sha(wl):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_reduce_amd", "csrc")
@@ -171,7 +185,7 @@ def roofline(wl, us):
                        "unit": "G wave64 VALU issues/s", "frac": round(ach / VALU_PEAK_GSLOTS, 4),
                        "issue_slots_per_launch": slots, "valu_insts_per_launch": c.get("valu_insts")}
         if c.get("clock_ghz"):                        # the same issue slots at the measured clock
-            peak_at = 256 * 4 * c["clock_ghz"] / 4
+            peak_at = 256 * 4 * c["clock_ghz"] / 2
             out["valu"].update(clock_ghz=c["clock_ghz"], peak_at_clock=round(peak_at, 1),
                                frac_at_clock=round(ach / peak_at, 4))
     if c.get("mfma_busy_frac") is not None:
@@ -389,6 +403,8 @@ def launch_stats(torch, stream, fn, n, warmup, batch=25):
 
 CAL_BYTES = 2 * 8192 * 4096          # one 64 MiB int16 tensor
 CAL_KERNEL = "BitwiseOr"               # name fragment of the calibration kernel
+AMAX_PASS = "amax_partial_kernel"      # the tensor-amax pass of a full step
+AFTER_AMAX = " (after the amax pass)"
 
 
 def copy_reference(torch, row):
@@ -584,21 +600,35 @@ def summarize(out_path, dirs, command):
             c = sqlite3.connect(db)
             tabs = {r[0] for r in c.execute("select name from sqlite_master")}
             if "kernels" in tabs:
-                for n, dur in c.execute("select name, duration from kernels"):
-                    durations.setdefault(short(n), []).append(dur / 1000.0)
+                # a launch that directly follows an amax pass re-reads what that
+                # pass just read (a full quantization step): listed apart
+                prev = ""
+                for n, dur, g in c.execute("select name, duration, grid_x * grid_y * grid_z "
+                                           "from kernels order by start"):
+                    k = short(n)
+                    if prev.startswith(AMAX_PASS) and not k.startswith(AMAX_PASS):
+                        k += AFTER_AMAX
+                    durations.setdefault((k, g), []).append(dur / 1000.0)
+                    prev = short(n)
             if "counters_collection" in tabs:
                 for n, cn, v, g in c.execute(
                         "select kernel_name, counter_name, value, grid_size from counters_collection"):
                     counters.setdefault((short(n), cn, g), []).append(v)
+    def wl_durations(wl, kern):                      # this workload's launches of its kernel
+        grid = expected_items(wl)
+        return [x for (k, g), v in durations.items() if k == kern and (grid is None or g == grid)
+                for x in v]
+
     lines = ["# rocprofv3 summary", "", "Command:", "", "```", command, "```", ""]
     if durations:
-        lines += ["| kernel | launches | avg us | median us | p10 us | p90 us | min us | max us |",
-                  "|---|---|---|---|---|---|---|---|"]
-        for k, v in sorted(durations.items(), key=lambda kv: -sum(kv[1])):
+        lines += ["| kernel | work-items | launches | avg us | median us | p10 us | p90 us | "
+                  "min us | max us |", "|---|---|---|---|---|---|---|---|---|"]
+        for (k, g), v in sorted(durations.items(), key=lambda kv: -sum(kv[1])):
             sv = sorted(v)
             pq = lambda f: sv[min(len(sv) - 1, int(round(f * (len(sv) - 1))))]
-            lines.append("| %s | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
-                k, len(v), sum(v) / len(v), statistics.median(v), pq(0.1), pq(0.9), min(v), max(v)))
+            lines.append("| %s | %d | %d | %.2f | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+                k, g, len(v), sum(v) / len(v), statistics.median(v), pq(0.1), pq(0.9), min(v),
+                max(v)))
         lines.append("")
     merged = {}
     if os.path.exists(COUNTERS_FILE):
@@ -621,8 +651,9 @@ def summarize(out_path, dirs, command):
                   "VALU insts | VALU issue slots |", "|---|---|---|---|---|---|---|"]
         for wl, kern in KERNEL_OF.items():
             q = {}
+            grid = expected_items(wl)
             for (k, cn, g), v in counters.items():
-                if k.startswith(kern):
+                if k.startswith(kern) and (grid is None or g == grid):
                     q.setdefault(cn, []).extend(v)
             q = {cn: sum(v) / len(v) for cn, v in q.items()}
             if not q:
@@ -643,15 +674,16 @@ def summarize(out_path, dirs, command):
                 e["valu_insts"] = round(q["SQ_INSTS_VALU"])
             if "SQ_ACTIVE_INST_VALU" in q:            # wave64 VALU issues (8-cycle ones count 2)
                 e["valu_issue_slots"] = round(q["SQ_ACTIVE_INST_VALU"])
-            if kern in durations:
-                e["avg_us_trace"] = round(sum(durations[kern]) / len(durations[kern]), 3)
+            dur = wl_durations(wl, kern)
+            if dur:
+                e["avg_us_trace"] = round(sum(dur) / len(dur), 3)
             # shader clock over the kernel: GRBM_GUI_ACTIVE counts busy cycles
             # on each of the 8 XCDs over the profiled dispatch, which adds a
             # few us of launch and drain to the kernel's duration, so the
             # figure is kept for kernels of 150 us and more only (there the
             # excess is under 2 %)
-            if "GRBM_GUI_ACTIVE" in q and kern in durations:
-                us = statistics.median(durations[kern])
+            if "GRBM_GUI_ACTIVE" in q and dur:
+                us = statistics.median(dur)
                 if us >= 150.0:
                     e["clock_ghz"] = round(q["GRBM_GUI_ACTIVE"] / 8 / (us * 1e3), 3)
             # matrix-core busy cycles (summed over SIMDs) over the CU busy
@@ -667,8 +699,9 @@ def summarize(out_path, dirs, command):
                 e.get("valu_insts", "-"), e.get("valu_issue_slots", "-")))
     elif durations:
         for wl, kern in KERNEL_OF.items():
-            if kern in durations and wl in merged and merged[wl].get("sources_sha") == sources_sha(wl):
-                merged[wl]["avg_us_trace"] = round(sum(durations[kern]) / len(durations[kern]), 3)
+            dur = wl_durations(wl, kern)
+            if dur and wl in merged and merged[wl].get("sources_sha") == sources_sha(wl):
+                merged[wl]["avg_us_trace"] = round(sum(dur) / len(dur), 3)
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     if merged:
