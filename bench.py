@@ -135,17 +135,17 @@ def algorithmic_bytes(wl):
 
 
 def expected_items(wl):
-    """Work-items of the workload's quantize launch, for the 1D quantizer
-    (whose kernel c1 shares with the same-traffic RTN6 reference row, so a
-    profile tells them apart by launch size only); None for other kernels.
-    Follows the 1D launch rule: one 256-thread workgroup per 256 blocks, at
-    most 6 (4 with SR) resident per CU of the 256."""
+    """Work-items of the workload's quantize launch where a profile can tell
+    it apart from another row's by launch size only: the 1D RTN6 quantizer,
+    which c1 shares with the same-traffic RTN6 reference row.  Follows the
+    1D launch rule without SR: one 256-thread workgroup per 256 blocks, at
+    most 6 per CU of the 256.  None for every other workload (its kernel
+    instance is its own)."""
     rows, cols, kind, flags, _ = ROWS[wl]
-    if kind != "nvfp4" or flags & (8 | 128):
+    if kind != "nvfp4" or flags:
         return None
     nblocks = rows * cols // 16
-    per_cu = 4 if flags & 2 else 6
-    return min(-(-nblocks // 256), 256 * per_cu) * 256
+    return min(-(-nblocks // 256), 256 * 6) * 256
 
 
 def sources_sha(wl):

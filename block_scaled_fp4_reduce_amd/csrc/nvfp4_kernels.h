@@ -34,7 +34,7 @@ namespace fp4q {
 #define FP4Q_BPT 1
 #endif
 #ifndef FP4Q_WG_PER_CU
-#define FP4Q_WG_PER_CU 4
+#define FP4Q_WG_PER_CU 12
 #endif
 #ifndef FP4Q_HW_E4M3
 #define FP4Q_HW_E4M3 1
@@ -43,11 +43,16 @@ constexpr int kAmaxMaxGroups = FP4Q_AMAX_GROUPS;
 constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
 constexpr int kAmaxThreads = FP4Q_AMAX_THREADS;
 constexpr int kBpt = FP4Q_BPT;              // 16-value blocks per lane per chunk (1D quantizer)
-constexpr int kWgPerCu = FP4Q_WG_PER_CU;    // resident 1D-quantizer workgroups per CU
+// Workgroups launched per CU by the 1D quantizer with SR and by MS-EDEN.
+// Their Philox work needs about 100 VGPRs, so four waves per SIMD are
+// resident; launching three times as many workgroups as fit (the others
+// start as the first ones finish) evens out the end of the grid, where a
+// fixed split leaves the CUs that hold the youngest workgroups busy last
+// (8192x14336 RHT16 + SR: 175 -> 170 us; MS-EDEN: 61 -> 59 us).
+constexpr int kWgPerCu = FP4Q_WG_PER_CU;
 // Without SR the 1D quantizer needs at most 64 VGPRs, so six 4-wave
 // workgroups fit per CU (six waves per SIMD), which covers its loads better
-// than four (8192x4096 4/6: quantize 17.3 -> 16.4 us); the SR variants need
-// about 100 VGPRs for Philox, so four waves per SIMD is all that fits.
+// than four (8192x4096 4/6: quantize 17.3 -> 16.4 us).
 #ifndef FP4Q_WG_PER_CU_NOSR
 #define FP4Q_WG_PER_CU_NOSR 6
 #endif

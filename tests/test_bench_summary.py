@@ -24,7 +24,7 @@ def _db(path):
               "grid_y integer, grid_z integer, start integer)")
     c.execute("create table counters_collection (kernel_name text, counter_name text, "
               "value real, grid_size integer)")
-    small, big, f46 = bench.expected_items("c1"), 393216, bench.expected_items("c2")
+    small, big, f46 = bench.expected_items("c1"), 393216, 393216
     launches = []
     for _ in range(3):
         launches += [(RTN6, 3000, small), (RTN6, 16000, big), (F46, 17000, f46)]
@@ -45,9 +45,9 @@ def _db(path):
 
 def test_expected_items_follow_the_1d_launch_rule():
     assert bench.expected_items("c1") == 64 * 256          # 16384 blocks: 64 workgroups
-    assert bench.expected_items("c2") == 1536 * 256        # capped at 6 per CU
-    assert bench.expected_items("c4") == 1024 * 256        # SR: 4 per CU
-    assert bench.expected_items("c3") is None              # 2D: its own kernel
+    assert bench.expected_items("c2") is None              # 4/6: its own kernel instance
+    assert bench.expected_items("c4") is None
+    assert bench.expected_items("c3") is None
 
 
 def test_shared_kernel_split_by_launch_size(tmp_path, monkeypatch):
