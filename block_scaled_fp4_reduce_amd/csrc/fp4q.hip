@@ -142,26 +142,26 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
     if (g >= 8) g -= g % 8;
     return g < 1 ? (int64_t)1 : g;
   };
-  const int64_t resident = (int64_t)num_cus() * kRqWgPerCu;
+  const int64_t launched = (int64_t)num_cus() * kRqWgPerCu;
   const uint32_t* abits = (const uint32_t*)amax_in;
   int namax = 1;
   hipError_t e = hipSuccess;
   if (!amax_in) {
-    const int64_t ga = grid(resident < kRqAmaxGroups ? resident : kRqAmaxGroups);
+    const int64_t ga = grid(launched < kRqAmaxGroups ? launched : kRqAmaxGroups);
     e = launch(rq_amax_kernel<RHT>, (unsigned)ga, kRqThreads, st, codes, scales, alpha, rows,
                cols, TY, TX, ws, lo, hi);
     abits = ws;
     namax = (int)ga;
   }
-  return first(e, launch(rq_quant_kernel<F46, SR, RHT>, (unsigned)grid(resident), kRqThreads, st,
+  return first(e, launch(rq_quant_kernel<F46, SR, RHT>, (unsigned)grid(launched), kRqThreads, st,
                          codes, scales, alpha, rows, cols, TY, TX, abits, namax, alpha_out,
                          codes_t, scales_t, choice_t, lo, hi));
 }
 
-// Persistent grid: as many workgroups of `kernel` as fit on the chip at
-// once (its register use sets that; queried once per kernel), at most
-// `want`.
-int64_t resident_grid(const void* kernel, int& per_cu, int64_t want) {
+// Persistent grid: `over` times as many workgroups of `kernel` as fit on
+// the chip at once (its register use sets that; queried once per kernel),
+// at most `want`.
+int64_t resident_grid(const void* kernel, int& per_cu, int64_t want, int over = 1) {
   if (per_cu == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kRowThreads, 0) != hipSuccess ||
@@ -169,7 +169,7 @@ int64_t resident_grid(const void* kernel, int& per_cu, int64_t want) {
       n = 2;
     per_cu = n < kRowWgPerCu ? n : kRowWgPerCu;
   }
-  const int64_t cap = (int64_t)num_cus() * per_cu;
+  const int64_t cap = (int64_t)num_cus() * per_cu * over;
   int64_t g = want < cap ? want : cap;
   return g < 1 ? 1 : g;
 }
@@ -191,7 +191,8 @@ hipError_t launch_rows_wg(const uint16_t* x, int64_t rows, int64_t cols, float* 
                           hipStream_t st) {
   static int per_cu = 0;
   const int64_t grid =
-      resident_grid((const void*)nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, per_cu, rows);
+      resident_grid((const void*)nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, per_cu, rows,
+                    kRowWgLaunch);
   return launch(nvfp4_rows_wg_kernel<F46, SR, RHT, NB, ONE>, (unsigned)grid, kRowThreads, st, x,
                 rows, cols, alpha_rows, codes, scales, choice, (uint32_t)seed,
                 (uint32_t)(seed >> 32));
