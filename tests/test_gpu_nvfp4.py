@@ -115,10 +115,20 @@ def test_parity_chunk_order(shape, flags):
     """Unrotated shapes whose grid is a multiple of 8, so the workgroups take
     their chunks in the amax pass's XCD order: 1000 chunks (a grid of 1000,
     a chunk count that is not a multiple of 64) and 1607 chunks with a
-    partial last one (a grid of 1536 on 256 CUs without SR, 1024 with SR).
-    Every chunk must be quantized once, the SR counter must stay the element
-    index."""
+    partial last one (a grid of 1536 on 256 CUs without SR; with SR every
+    chunk gets a workgroup of its own).  Every chunk must be quantized once,
+    the SR counter must stay the element index."""
     run_case(S.gen("c2", *shape), flags)
+
+
+@pytest.mark.parametrize("flags", [fp4.SR, fp4.RHT16 | fp4.SR, fp4.RHT16 | fp4.MSEDEN])
+@pytest.mark.parametrize("rows", [3071, 3073, 6145])
+def test_parity_launch_edges(rows, flags):
+    """Chunk counts (a chunk is 4096 values: one 4096-value row here) around
+    the 3072 workgroups the SR and MS-EDEN kernels launch on 256 CUs (twelve
+    per CU, four resident): one chunk each with one workgroup idle, one
+    workgroup taking a second chunk, and every workgroup two or three."""
+    run_case(S.gen("c4", rows, 4096), flags)
 
 
 def test_tensor_amax():

@@ -67,6 +67,17 @@ def test_requant_random_bytes(shape, flags):
     run_case(codes, scales, 0.0137, flags, ctx="random")
 
 
+@pytest.mark.parametrize("flags", [fp4.FOUR_OVER_SIX, fp4.RHT16 | fp4.SR])
+@pytest.mark.parametrize("ntiles", [1023, 1025, 2049])
+def test_requant_launch_edges(ntiles, flags):
+    """Tile counts around the 1024 workgroups the requantization launches on
+    256 CUs (four per CU, two resident): a 16-row input has one 16x256 tile
+    per 256 columns, so every workgroup takes one tile, one takes a second,
+    or all take two or three (the persistent tile loop and its XCD order)."""
+    codes, scales = S.random_nvfp4(16, 256 * ntiles - 240, seed=13)
+    run_case(codes, scales, 0.0137, flags, ctx="launch-edge")
+
+
 @pytest.mark.parametrize("flags", FLAG_SETS)
 def test_requant_of_quantized_activation(flags):
     codes, scales, alpha = quantized("c2", 528, 1296)

@@ -57,6 +57,16 @@ def test_rows_special_values(flags):
     run_case(S.special_values_tensor(48, 272), flags, ctx="special")
 
 
+@pytest.mark.parametrize("flags", [fp4.FOUR_OVER_SIX, fp4.RHT16 | fp4.SR])
+@pytest.mark.parametrize("rows", [4607, 4609, 9217])
+def test_rows_launch_edges(rows, flags):
+    """Row counts around the workgroups the workgroup-per-row kernel launches
+    for 4096-value rows (three times those resident: 4608 on 256 CUs at six
+    per CU): one row each with one workgroup idle, one workgroup taking a
+    second row, and every workgroup two or three."""
+    run_case(S.gen("c2", rows, 4096), flags, ctx="launch-edge")
+
+
 def test_rows_edge_shapes():
     run_case(S.gen("c2", 1, 16), fp4.FOUR_OVER_SIX, ctx="one block")
     run_case(S.gen("c2", 3, 16400), fp4.FOUR_OVER_SIX, ctx="three sweeps")
