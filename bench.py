@@ -408,17 +408,23 @@ AFTER_AMAX = " (after the amax pass)"
 
 
 def copy_reference(torch, row):
-    """Plain device copy of one input: the achievable bandwidth on this machine.
-    Also runs, a few times, a 64 MiB elementwise bitwise-or (reads exactly
-    CAL_BYTES, writes exactly CAL_BYTES) whose kernel name is unique in a
-    profile: rocprofv3 FETCH_SIZE / WRITE_SIZE of the quantizers are scaled
-    by what the counters read for it."""
-    src, dst = row.xs[1], row.xs[2].clone()
-    ms, _ = time_loop(torch, row.stream, lambda i: dst.copy_(src), 20, 3)
+    """Plain device copy of one input, from and to buffers that rotate over
+    1.5 GiB (so neither side is still in the 256 MB last-level cache): the
+    bandwidth a 1:1 read/write stream reaches on this machine.  Also runs, a few
+    times, a 64 MiB elementwise bitwise-or (reads exactly CAL_BYTES, writes
+    exactly CAL_BYTES) whose kernel name is unique in a profile: rocprofv3
+    FETCH_SIZE / WRITE_SIZE of the quantizers are scaled by what the
+    counters read for it."""
+    srcs = row.xs
+    dsts = [torch.empty_like(srcs[0]) for _ in range(8)]
+    ms, _ = time_loop(torch, row.stream,
+                      lambda i: dsts[i % len(dsts)].copy_(srcs[i % len(srcs)]), 24, 3)
     for _ in range(3):
-        torch.bitwise_or(src, 0, out=dst)
+        torch.bitwise_or(srcs[1], 0, out=dsts[0])
     torch.cuda.synchronize()
-    return 2 * src.numel() * 2 / (ms * 1e-3) / 1e9
+    gbs = 2 * srcs[0].numel() * 2 / (ms * 1e-3) / 1e9
+    del dsts
+    return gbs
 
 
 # ------------------------------------------------------------------ CPU side
