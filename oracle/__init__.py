@@ -92,6 +92,16 @@ def lib():
         L.orc_nvfp4_quantize_rows.restype = C.c_int
         L.orc_nvfp4_quantize_rows.argtypes = [u16p, C.c_int64, C.c_int64, C.c_uint32, C.c_uint64,
                                               f32p, u8p, u8p, u8p]
+        L.orc_nvfp4_quantize_at.restype = C.c_int
+        L.orc_nvfp4_quantize_at.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int64, C.c_uint32,
+                                            C.c_uint64, f32p, f32p, u8p, u8p, u8p]
+        L.orc_nvfp4_quantize_rows_at.restype = C.c_int
+        L.orc_nvfp4_quantize_rows_at.argtypes = [u16p, C.c_int64, C.c_int64, C.c_int64,
+                                                 C.c_uint32, C.c_uint64, f32p, u8p, u8p, u8p]
+        L.orc_nvfp4_requantize_t_at.restype = C.c_int
+        L.orc_nvfp4_requantize_t_at.argtypes = [u8p, u8p, C.c_float, C.c_int64, C.c_int64,
+                                                C.c_int64, C.c_uint32, C.c_uint64, f32p, f32p,
+                                                u8p, u8p, u8p]
         L.orc_nvfp4_requantize_t.restype = C.c_int
         L.orc_nvfp4_requantize_t.argtypes = [u8p, u8p, C.c_float, C.c_int64, C.c_int64,
                                              C.c_uint32, C.c_uint64, f32p, u8p, u8p, u8p]
@@ -230,6 +240,27 @@ def nvfp4_quantize(x_bf16, flags=0, seed=0, amax=None, debug=False):
     return out
 
 
+def nvfp4_quantize_at(x_bf16, row0, amax, flags=0, seed=0):
+    """nvfp4_quantize (1D flags) of rows row0 .. row0 + len(x) - 1 of a larger
+    tensor, given alone: SR and MS-EDEN draw with the whole tensor's element
+    and block indices, and `amax` is the whole tensor's.  row0 = 0 is
+    nvfp4_quantize(x, flags, seed, amax)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    choice = np.zeros((rows, cols // 16), np.uint8)
+    alpha = np.zeros(1, np.float32)
+    amax_arr = np.array([amax], np.float32)
+    rc = lib().orc_nvfp4_quantize_at(
+        _p(x, C.c_uint16), rows, cols, int(row0), flags, C.c_uint64(seed & (2**64 - 1)),
+        _p(amax_arr, C.c_float), _p(alpha, C.c_float), _p(codes, C.c_uint8),
+        _p(scales, C.c_uint8), _p(choice, C.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle nvfp4_quantize_at rejected the arguments (%d)" % rc)
+    return dict(codes=codes, scales=scales, alpha=np.float32(alpha[0]), choice=choice)
+
+
 def nvfp4_quantize_f32(x_f32, flags=0, seed=0, amax=None):
     """NVFP4 of an fp32 tensor (1D flags); dict(codes, scales, alpha, choice)."""
     x = np.ascontiguousarray(x_f32, dtype=np.float32)
@@ -265,6 +296,23 @@ def nvfp4_quantize_rows(x_bf16, flags=0, seed=0):
     return {"codes": codes, "scales": scales, "alpha": alpha[:rows], "choice": choice}
 
 
+def nvfp4_quantize_rows_at(x_bf16, row0, flags=0, seed=0):
+    """nvfp4_quantize_rows of rows row0 .. row0 + len(x) - 1 of a larger
+    tensor, given alone (SR counters are the whole tensor's element indices)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    choice = np.zeros((rows, cols // 16), np.uint8)
+    alpha = np.zeros(max(rows, 1), np.float32)
+    rc = lib().orc_nvfp4_quantize_rows_at(
+        _p(x, C.c_uint16), rows, cols, int(row0), flags, C.c_uint64(seed & (2**64 - 1)),
+        _p(alpha, C.c_float), _p(codes, C.c_uint8), _p(scales, C.c_uint8), _p(choice, C.c_uint8))
+    if rc != 0:
+        raise ValueError("orc_nvfp4_quantize_rows_at failed: %d" % rc)
+    return {"codes": codes, "scales": scales, "alpha": alpha[:rows], "choice": choice}
+
+
 def nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags=0, seed=0):
     """NVFP4 (flags) of dequantize(X)^T for a 1D NVFP4 X [rows][cols]:
     dict(codes [cols][rows/2], scales [cols][rows/16], alpha, choice)."""
@@ -280,6 +328,27 @@ def nvfp4_requantize_t(codes, scales, alpha, rows, cols, flags=0, seed=0):
         _p(ch, C.c_uint8))
     if rc != 0:
         raise ValueError("oracle nvfp4_requantize_t rejected the arguments (%d)" % rc)
+    return dict(codes=ct, scales=st, alpha=np.float32(a[0]), choice=ch)
+
+
+def nvfp4_requantize_t_at(codes, scales, alpha, rows, cols, col0, amax, flags=0, seed=0):
+    """nvfp4_requantize_t of columns col0 .. col0 + cols - 1 of a larger X
+    (their codes [rows][cols/2] and scales [rows][cols/16]): output rows
+    col0 .. of the whole transpose, given the whole output's amax; SR draws
+    with the whole output's element indices."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    ct = np.zeros((cols, rows // 2), np.uint8)
+    st = np.zeros((cols, rows // 16), np.uint8)
+    ch = np.zeros((cols, rows // 16), np.uint8)
+    a = np.zeros(1, np.float32)
+    amax_arr = np.array([amax], np.float32)
+    rc = lib().orc_nvfp4_requantize_t_at(
+        _p(codes, C.c_uint8), _p(scales, C.c_uint8), C.c_float(alpha), rows, cols, int(col0),
+        flags, C.c_uint64(seed & (2**64 - 1)), _p(amax_arr, C.c_float), _p(a, C.c_float),
+        _p(ct, C.c_uint8), _p(st, C.c_uint8), _p(ch, C.c_uint8))
+    if rc != 0:
+        raise ValueError("oracle nvfp4_requantize_t_at rejected the arguments (%d)" % rc)
     return dict(codes=ct, scales=st, alpha=np.float32(a[0]), choice=ch)
 
 

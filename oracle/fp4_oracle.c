@@ -25,6 +25,9 @@
  *                                         quantizer on that row alone)
  *   error-study simulation .............. pinned (no switch = dequantize of
  *                                         the quantizer, sweep end points)
+ *   row / column bands of a larger tensor  pinned (equal to the whole-tensor
+ *                                         results for those rows; a wrong
+ *                                         offset changes the random draws)
  *   MS-EDEN ............................. partly pinned: the unbiasing factor
  *                                         is not on the pages (EDEN's is taken);
  *                                         its projection property, nearest
@@ -450,7 +453,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
                               uint32_t flags, uint64_t seed, const float* amax_in,
                               float* alpha_out, uint8_t* codes, uint8_t* scales,
                               uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
-                              orc_debug* dbg, int rowscale) {
+                              orc_debug* dbg, int rowscale, int64_t row0) {
   if (!nvfp4_flags_ok(rows, cols, flags)) return -1;
   if (!codes || !scales || !alpha_out) return -2;
   const int two_d = (flags & ORC_BLOCK2D) != 0;
@@ -504,7 +507,7 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
         const int64_t r = two_d ? br * 16 + i / 16 : br;
         const int64_t c = bc * 16 + (i % 16);
         elems[i] = &y[r * cols + c];
-        idx[i] = (uint64_t)(r * cols + c);
+        idx[i] = (uint64_t)((row0 + r) * cols + c);   /* index in the whole tensor */
         const float a = fabsf(*elems[i]);
         if (a > amax_b) amax_b = a;
       }
@@ -512,7 +515,8 @@ static int nvfp4_quantize_any(const uint16_t* x, const float* xf, int64_t rows, 
         float yb[16];
         for (int i = 0; i < 16; i++) yb[i] = *elems[i];
         const int64_t bidx = br * bcols + bc;
-        scales[bidx] = quantize_block_msed(yb, amax_b, sc.alpha, sc.k6, seed, (uint64_t)bidx,
+        scales[bidx] = quantize_block_msed(yb, amax_b, sc.alpha, sc.k6, seed,
+                                           (uint64_t)((row0 + br) * bcols + bc),
                                            c6, dbg && dbg->dpre6 ? &dbg->dpre6[bidx] : NULL);
         if (choice) choice[bidx] = 0;
         for (int i = 0; i < 16; i++) put_nibble(&codes[br * (cols / 2)], bc * 16 + i, c6[i]);
@@ -564,7 +568,22 @@ int orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
                        orc_debug* dbg) {
   if (!x && rows * cols > 0) return -2;
   return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, amax_in, alpha_out, codes,
-                            scales, choice, codes_t, scales_t, dbg, 0);
+                            scales, choice, codes_t, scales_t, dbg, 0, 0);
+}
+
+/* orc_nvfp4_quantize (1D flags) of rows row0 .. row0 + rows - 1 of a larger
+ * tensor with `cols` columns, given here alone: the random counters (SR:
+ * element index; MS-EDEN: block index) are those of the whole tensor, and
+ * amax_in must be the whole tensor's.  With row0 = 0 it is
+ * orc_nvfp4_quantize. */
+int orc_nvfp4_quantize_at(const uint16_t* x, int64_t rows, int64_t cols, int64_t row0,
+                          uint32_t flags, uint64_t seed, const float* amax_in,
+                          float* alpha_out, uint8_t* codes, uint8_t* scales,
+                          uint8_t* choice) {
+  if (!x && rows * cols > 0) return -2;
+  if (row0 < 0 || !amax_in || (flags & (ORC_BLOCK2D | ORC_COLWISE))) return -1;
+  return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, amax_in, alpha_out, codes,
+                            scales, choice, NULL, NULL, NULL, 0, row0);
 }
 
 int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t flags,
@@ -573,7 +592,7 @@ int orc_nvfp4_quantize_f32(const float* x, int64_t rows, int64_t cols, uint32_t 
   if (!x && rows * cols > 0) return -2;
   if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
   return nvfp4_quantize_any(NULL, x, rows, cols, flags, seed, amax_in, alpha_out, codes,
-                            scales, choice, NULL, NULL, NULL, 0);
+                            scales, choice, NULL, NULL, NULL, 0, 0);
 }
 
 /* NVFP4 with one FP32 scale per row instead of per tensor: the finer
@@ -588,7 +607,18 @@ int orc_nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint3
   if (!x && rows * cols > 0) return -2;
   if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
   return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, NULL, alpha_rows, codes, scales,
-                            choice, NULL, NULL, NULL, 1);
+                            choice, NULL, NULL, NULL, 1, 0);
+}
+
+/* orc_nvfp4_quantize_rows of rows row0 .. row0 + rows - 1 of a larger tensor
+ * (each row's scale is its own, so only the SR counters need row0). */
+int orc_nvfp4_quantize_rows_at(const uint16_t* x, int64_t rows, int64_t cols, int64_t row0,
+                               uint32_t flags, uint64_t seed, float* alpha_rows,
+                               uint8_t* codes, uint8_t* scales, uint8_t* choice) {
+  if (!x && rows * cols > 0) return -2;
+  if (row0 < 0 || (flags & (ORC_BLOCK2D | ORC_COLWISE))) return -1;
+  return nvfp4_quantize_any(x, NULL, rows, cols, flags, seed, NULL, alpha_rows, codes, scales,
+                            choice, NULL, NULL, NULL, 1, row0);
 }
 
 /* Requantization for the transposed operand of the backward pass ([QII]
@@ -599,11 +629,11 @@ int orc_nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t cols, uint3
  * dequantized values: quantize((dequantize(X))^T), blocks of 16 running
  * along the original columns.  Output: codes_t [cols][rows/2], scales_t
  * [cols][rows/16], choice_t likewise (may be NULL). */
-int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float alpha,
-                           int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
-                           float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
-                           uint8_t* choice_t) {
-  if (rows < 0 || cols < 0 || rows % 16 || cols % 16) return -1;
+static int requantize_t_any(const uint8_t* codes, const uint8_t* scales, float alpha,
+                            int64_t rows, int64_t cols, int64_t col0, uint32_t flags,
+                            uint64_t seed, const float* amax_in, float* alpha_out,
+                            uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t) {
+  if (rows < 0 || cols < 0 || rows % 16 || cols % 16 || col0 < 0) return -1;
   if (flags & (ORC_BLOCK2D | ORC_COLWISE)) return -1;
   const size_t n = (size_t)(rows * cols > 0 ? rows * cols : 1);
   float* xd = (float*)malloc(sizeof(float) * n);
@@ -613,12 +643,33 @@ int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float al
   if (rc == 0) {
     for (int64_t r = 0; r < rows; r++)
       for (int64_t c = 0; c < cols; c++) xt[c * rows + r] = xd[r * cols + c];
-    rc = nvfp4_quantize_any(NULL, xt, cols, rows, flags, seed, NULL, alpha_out, codes_t,
-                            scales_t, choice_t, NULL, NULL, NULL, 0);
+    rc = nvfp4_quantize_any(NULL, xt, cols, rows, flags, seed, amax_in, alpha_out, codes_t,
+                            scales_t, choice_t, NULL, NULL, NULL, 0, col0);
   }
   free(xd);
   free(xt);
   return rc;
+}
+
+int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float alpha,
+                           int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
+                           float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
+                           uint8_t* choice_t) {
+  return requantize_t_any(codes, scales, alpha, rows, cols, 0, flags, seed, NULL, alpha_out,
+                          codes_t, scales_t, choice_t);
+}
+
+/* orc_nvfp4_requantize_t of columns col0 .. col0 + cols - 1 of a larger X
+ * (codes and scales of those columns, all rows): output rows col0 .. of the
+ * whole transpose, whose amax (amax_in, required) and SR element indices
+ * are the whole output tensor's. */
+int orc_nvfp4_requantize_t_at(const uint8_t* codes, const uint8_t* scales, float alpha,
+                              int64_t rows, int64_t cols, int64_t col0, uint32_t flags,
+                              uint64_t seed, const float* amax_in, float* alpha_out,
+                              uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t) {
+  if (!amax_in) return -1;
+  return requantize_t_any(codes, scales, alpha, rows, cols, col0, flags, seed, amax_in,
+                          alpha_out, codes_t, scales_t, choice_t);
 }
 
 /* ===================================================================== */

@@ -113,6 +113,20 @@ int orc_nvfp4_quantize_rows(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                             uint32_t flags, uint64_t seed, float* alpha_rows,
                             uint8_t* codes, uint8_t* scales, uint8_t* choice);
 
+/* The two above (1D flags) on rows row0 .. row0 + rows - 1 of a larger
+ * tensor with `cols` columns, passed alone: the random counters (SR element
+ * index, MS-EDEN block index) are the whole tensor's, and orc_nvfp4_quantize_at
+ * takes the whole tensor's amax (amax_in, required).  row0 = 0 gives the
+ * functions above. */
+int orc_nvfp4_quantize_at(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t row0,
+                          uint32_t flags, uint64_t seed, const float* amax_in,
+                          float* alpha_out, uint8_t* codes, uint8_t* scales,
+                          uint8_t* choice);
+int orc_nvfp4_quantize_rows_at(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                               int64_t row0, uint32_t flags, uint64_t seed,
+                               float* alpha_rows, uint8_t* codes, uint8_t* scales,
+                               uint8_t* choice);
+
 /* Requantize a 1D NVFP4 tensor X [rows][cols] (codes, scales, alpha) for the
  * transposed operand: NVFP4 (flags as above) of dequantize(X)^T, giving
  * codes_t [cols][rows/2], scales_t [cols][rows/16], choice_t (or NULL).
@@ -122,6 +136,15 @@ int orc_nvfp4_requantize_t(const uint8_t* codes, const uint8_t* scales, float al
                            int64_t rows, int64_t cols, uint32_t flags, uint64_t seed,
                            float* alpha_out, uint8_t* codes_t, uint8_t* scales_t,
                            uint8_t* choice_t);
+
+/* orc_nvfp4_requantize_t of columns col0 .. col0 + cols - 1 of a larger X
+ * (their codes [rows][cols/2] and scales [rows][cols/16], all rows): output
+ * rows col0 .. col0 + cols - 1 of the whole transpose, with the whole output
+ * tensor's amax (amax_in, required) and its SR element indices. */
+int orc_nvfp4_requantize_t_at(const uint8_t* codes, const uint8_t* scales, float alpha,
+                              int64_t rows, int64_t cols, int64_t col0, uint32_t flags,
+                              uint64_t seed, const float* amax_in, float* alpha_out,
+                              uint8_t* codes_t, uint8_t* scales_t, uint8_t* choice_t);
 
 /* Dequantization. format 0 = NVFP4 (alpha used, BLOCK2D selects 16x16
  * tiles), 1 = MXFP4 (row-wise layout; pass the transposed shape for the
