@@ -53,11 +53,18 @@ int check_nvfp4_flags(uint32_t flags) {
   return FP4_OK;
 }
 
-int amax_groups(int64_t ngroups16) {
-  const int64_t per_group = (int64_t)kAmaxThreads * kAmaxUnroll;   // uint4 loads per workgroup pass
+// The amax pass with the 1D quantizer's smaller workgroups: neither 2D
+// tiles nor the rotation (whose pass is bound by the butterflies).
+bool amax_one_d(uint32_t flags) { return !(flags & (FP4_BLOCK2D | FP4_RHT16)); }
+
+// Workgroups of the amax pass: the 1D quantizer's (one_d) or the others'.
+int amax_groups(int64_t ngroups16, bool one_d) {
+  const int64_t per_group =                                          // uint4 loads per workgroup pass
+      (int64_t)(one_d ? kAmaxThreads1d : kAmaxThreads) * kAmaxUnroll;
+  const int64_t cap = one_d ? kAmaxMaxGroups1d : kAmaxMaxGroups;
   int64_t g = cdiv(ngroups16 * 2, per_group);
   if (g < 1) g = 1;
-  if (g > kAmaxMaxGroups) g = kAmaxMaxGroups;
+  if (g > cap) g = cap;
   return (int)g;
 }
 
@@ -84,13 +91,17 @@ int num_cus() {
 
 // Queue the amax pass: partial maxima into ws (as uint32), `groups` of them.
 hipError_t launch_amax_partial(const uint16_t* x, int64_t ngroups16, uint32_t flags,
-                               uint64_t seed, uint32_t* ws, int groups, hipStream_t st) {
+                               uint64_t seed, uint32_t* ws, int groups, bool one_d,
+                               hipStream_t st) {
   const uint32_t lo = (uint32_t)seed, hi = (uint32_t)(seed >> 32);
-  if (flags & FP4_RHT16)
-    return launch(amax_partial_kernel<true>, groups, kAmaxThreads, st, (const uint4*)x, ngroups16,
-                  ws, lo, hi);
-  return launch(amax_partial_kernel<false>, groups, kAmaxThreads, st, (const uint4*)x, ngroups16,
-                ws, lo, hi);
+  if (flags & FP4_RHT16)                 // one_d is false here (amax_one_d)
+    return launch(amax_partial_kernel<true, kAmaxThreads>, groups, kAmaxThreads, st,
+                  (const uint4*)x, ngroups16, ws, lo, hi);
+  if (one_d)
+    return launch(amax_partial_kernel<false, kAmaxThreads1d>, groups, kAmaxThreads1d, st,
+                  (const uint4*)x, ngroups16, ws, lo, hi);
+  return launch(amax_partial_kernel<false, kAmaxThreads>, groups, kAmaxThreads, st,
+                (const uint4*)x, ngroups16, ws, lo, hi);
 }
 
 template <bool F46, bool SR, bool RHT>
@@ -239,7 +250,7 @@ const char* fp4_status_str(int status) {
 size_t fp4_workspace_bytes(int64_t rows, int64_t cols, uint32_t flags) {
   (void)rows; (void)cols;
   if (flags & FP4_HAD32) return 0;
-  const int groups = kAmaxMaxGroups > kRqAmaxGroups ? kAmaxMaxGroups : kRqAmaxGroups;
+  const int groups = kAmaxMaxGroupsAll > kRqAmaxGroups ? kAmaxMaxGroupsAll : kRqAmaxGroups;
   return (size_t)groups * sizeof(uint32_t);
 }
 
@@ -254,8 +265,9 @@ int fp4_tensor_amax(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flag
   if (ws_bytes < fp4_workspace_bytes(rows, cols, flags)) return FP4_E_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int64_t ng = n / 16;
-  const int groups = amax_groups(ng);
-  const hipError_t e = launch_amax_partial(x, ng, flags, seed, (uint32_t*)ws, groups, st);
+  const bool one_d = amax_one_d(flags);
+  const int groups = amax_groups(ng, one_d);
+  const hipError_t e = launch_amax_partial(x, ng, flags, seed, (uint32_t*)ws, groups, one_d, st);
   return launched(first(e, launch(amax_finalize_kernel, 1, kThreads, st, (const uint32_t*)ws,
                                   groups, amax_out)));
 }
@@ -308,8 +320,9 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint32_t flags
   int namax = 1;
   hipError_t e = hipSuccess;
   if (!amax_in) {
-    namax = amax_groups(nblocks);
-    e = launch_amax_partial(x, nblocks, flags, seed, (uint32_t*)ws, namax, st);
+    const bool one_d = amax_one_d(flags);
+    namax = amax_groups(nblocks, one_d);
+    e = launch_amax_partial(x, nblocks, flags, seed, (uint32_t*)ws, namax, one_d, st);
     abits = (const uint32_t*)ws;
   }
   if (two_d) {
@@ -343,7 +356,7 @@ int nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols, uint32
                            uint64_t seed, const float* amax_in, float* alpha_out, uint8_t* codes,
                            uint8_t* scales, uint8_t* choice, uint8_t* codes_t, uint8_t* scales_t,
                            void* stream) {
-  static_assert(kAmaxMaxGroups * sizeof(uint32_t) <= kScratchBytes, "amax partials fit");
+  static_assert(kAmaxMaxGroupsAll * sizeof(uint32_t) <= kScratchBytes, "amax partials fit");
   if (amax_in)                           // no amax pass: no workspace at all
     return nvfp4_quantize(x, rows, cols, flags, seed, amax_in, alpha_out, codes, scales, choice,
                           codes_t, scales_t, nullptr, 0, stream);

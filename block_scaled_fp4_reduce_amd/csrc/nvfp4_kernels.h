@@ -30,6 +30,12 @@ namespace fp4q {
 #ifndef FP4Q_AMAX_UNROLL
 #define FP4Q_AMAX_UNROLL 4
 #endif
+#ifndef FP4Q_AMAX_THREADS_1D
+#define FP4Q_AMAX_THREADS_1D 512
+#endif
+#ifndef FP4Q_AMAX_GROUPS_1D
+#define FP4Q_AMAX_GROUPS_1D 512
+#endif
 #ifndef FP4Q_BPT
 #define FP4Q_BPT 1
 #endif
@@ -42,6 +48,13 @@ namespace fp4q {
 constexpr int kAmaxMaxGroups = FP4Q_AMAX_GROUPS;
 constexpr int kAmaxUnroll = FP4Q_AMAX_UNROLL;
 constexpr int kAmaxThreads = FP4Q_AMAX_THREADS;
+// The amax pass ahead of the 1D quantizer takes smaller workgroups: 512
+// threads on 32 KiB chunks, up to 512 of them (full 8192x4096 4/6 step
+// 25.8 -> 25.3 us); the 2D quantizer's step is faster after the larger ones
+// (62.8 against 63.7 us), so it and the rotated pass keep those.
+constexpr int kAmaxThreads1d = FP4Q_AMAX_THREADS_1D;
+constexpr int kAmaxMaxGroups1d = FP4Q_AMAX_GROUPS_1D;
+constexpr int kAmaxMaxGroupsAll = kAmaxMaxGroups > kAmaxMaxGroups1d ? kAmaxMaxGroups : kAmaxMaxGroups1d;
 constexpr int kBpt = FP4Q_BPT;              // 16-value blocks per lane per chunk (1D quantizer)
 // Workgroups launched per CU by the 1D quantizer with SR and by MS-EDEN.
 // Their Philox work needs about 100 VGPRs, so four waves per SIMD are
@@ -58,20 +71,20 @@ constexpr int kWgPerCu = FP4Q_WG_PER_CU;
 #endif
 constexpr int kWgPerCuNoSr = FP4Q_WG_PER_CU_NOSR;
 
-template <bool RHT>
-__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
+template <bool RHT, int THREADS>
+__global__ __launch_bounds__(THREADS) void amax_partial_kernel(
     const uint4* __restrict__ x, int64_t ngroups16, uint32_t* __restrict__ partials,
     uint32_t seed_lo, uint32_t seed_hi) {
-  __shared__ uint32_t red[kAmaxThreads / 64];
+  __shared__ uint32_t red[THREADS / 64];
   uint32_t m = 0;
   if constexpr (!RHT) {
     // Magnitude bits of two bf16 per dword; packed 16-bit integer max.
-    // Workgroups walk chunks of kAmaxThreads * kAmaxUnroll 16-byte vectors
+    // Workgroups walk chunks of THREADS * kAmaxUnroll 16-byte vectors
     // with a stride of the grid; a buffer resource per chunk makes loads
     // past the end read 0, so every load is issued unconditionally and the
     // next chunk is in flight while this one is reduced.
     typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    constexpr int64_t CH = (int64_t)kAmaxThreads * kAmaxUnroll;
+    constexpr int64_t CH = (int64_t)THREADS * kAmaxUnroll;
     const int64_t nvec = ngroups16 * 2;            // 8 bf16 per uint4
     const int64_t nch = (nvec + CH - 1) / CH;
     auto rsrc = [&](int64_t c) {
@@ -85,7 +98,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
       const __amdgpu_buffer_rsrc_t r = rsrc(c);
 #pragma unroll
       for (int u = 0; u < kAmaxUnroll; u++)
-        k.v[u] = buffer_load16(r, (u * kAmaxThreads + (int)threadIdx.x) * 16);
+        k.v[u] = buffer_load16(r, (u * THREADS + (int)threadIdx.x) * 16);
     };
     u16x2 mm = {0, 0};
     Chunk cur, nxt;
@@ -108,8 +121,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
     m = (lo > hi ? lo : hi) << 16;
   } else {
     const uint32_t signs = philox_w0(0u, 0u, 0u, 1u, seed_lo, seed_hi) & 0xFFFFu;
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    const int64_t g = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * THREADS;
+    const int64_t g = (int64_t)blockIdx.x * THREADS + threadIdx.x;
     float fm = 0.0f;
     for (int64_t i = g; i < ngroups16; i += stride) {
       const uint4 v0 = x[2 * i], v1 = x[2 * i + 1];
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(
     }
     m = __float_as_uint(fm);
   }
-  m = block_max_u32<kAmaxThreads>(m, red);
+  m = block_max_u32<THREADS>(m, red);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
@@ -442,25 +455,28 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
     return (cc >= 0 && cc < nchunks - 1) ? kThreads : (cc == nchunks - 1 && cc >= 0 ? tail : 0);
   };
   // Chunk order.  The amax pass leaves the last quarter or so of what each
-  // XCD read in that XCD's L2 (it takes 64 KiB chunks, chunk a on XCD a % 8
-  // when its grid is a multiple of 8, in rising order).  With a grid that is
-  // a multiple of 8, workgroups here take virtual chunk indices v = w + i G
-  // and map them so that XCD x gets exactly the 8 KiB chunks q with
-  // (q / 8) % 8 == x, highest first: k = (G/8) i + w/8 counts XCD x's chunks,
-  // q = 64 (top - k/8) + 8 x + k % 8.  The virtual range is padded to a
-  // multiple of 64; indices past the end map to chunks >= nchunks, which
-  // read and write nothing.  Not used with RHT16 (its amax pass walks the
-  // tensor in another order, and the kernel is ALU-bound).
+  // XCD read in that XCD's L2 (it takes chunks of R = 4 of these 8 KiB
+  // chunks, chunk a on XCD a % 8 when its grid is a multiple of 8, in rising
+  // order).  With a grid that is a multiple of 8, workgroups here take
+  // virtual chunk indices v = w + i G and map them so that XCD x gets
+  // exactly the 8 KiB chunks q with (q / R) % 8 == x, highest first:
+  // k = (G/8) i + w/8 counts XCD x's chunks, q = 8R (top - k/R) + R x + k % R.
+  // The virtual range is padded to a multiple of 8R; indices past the end
+  // map to chunks >= nchunks, which read and write nothing.  Not used with
+  // RHT16 (its amax pass walks the tensor in another order, and the kernel
+  // is ALU-bound).
+  constexpr int R = kAmaxThreads1d * kAmaxUnroll * 16 / (kThreads * 32);
+  static_assert(R >= 1 && (R & (R - 1)) == 0, "amax chunk: a power-of-two number of 8 KiB chunks");
   const bool remap_on = !RHT && (G & 7) == 0;
-  const int top = (nchunks - 1) >> 6;                  // -1 for an empty tensor
-  const int nvirt = remap_on ? 64 * (top + 1) : nchunks;
+  const int top = (nchunks - 1) / (8 * R);             // -1 for an empty tensor
+  const int nvirt = remap_on ? 8 * R * (top + 1) : nchunks;
   // v = blockIdx.x + i G is this workgroup's i-th virtual chunk
   const int k0 = (int)blockIdx.x >> 3, x0 = (int)blockIdx.x & 7, kstep = G >> 3;
   auto chunk_of = [&](int v, int i) {
     if (!remap_on) return v;
     if (v >= nvirt) return nchunks;                     // prefetch past the end: nothing
     const int k = kstep * i + k0;
-    return 64 * (top - (k >> 3)) + 8 * x0 + (k & 7);
+    return 8 * R * (top - k / R) + R * x0 + k % R;
   };
   auto in_rsrc = [&](int v, int i) {
     const int cc = chunk_of(v, i);
