@@ -131,12 +131,23 @@ def test_parity_launch_edges(rows, flags):
     run_case(S.gen("c4", rows, 4096), flags)
 
 
-def test_tensor_amax():
-    for flags in (0, fp4.RHT16):
-        x = S.gen("c4", 130, 4096)
-        a = fp4.fp4_tensor_amax(dev(x), flags, SEED)
+@pytest.mark.parametrize("flags", [0, fp4.RHT16, fp4.BLOCK2D])
+@pytest.mark.parametrize("shape", [(130, 4096), (16, 16), (4112, 4112), (8208, 4096)])
+def test_tensor_amax(shape, flags):
+    """Both forms of the amax pass (1D: 512-thread workgroups on 32 KiB
+    chunks; 2D and rotated: 1024 threads, 64 KiB), with partial last chunks
+    and more chunks than workgroups; the largest magnitude planted in the
+    tensor's last element, then elsewhere."""
+    x = S.gen("c4", *shape)
+    for pos in (x.size - 1, x.size // 3):
+        y = x.copy().reshape(-1)
+        y[pos] = 0xC2C8                                   # -100.0 in bf16
+        y = y.reshape(shape)
+        print("amax case", shape, "flags", flags, "pos", pos, flush=True)
+        a = fp4.fp4_tensor_amax(dev(y), flags, SEED)
         torch.cuda.synchronize()
-        assert host(a)[0] == np.float32(O.tensor_amax(x, flags, SEED))
+        # the oracle's amax takes only the rotation flag (2D tiles change nothing)
+        assert host(a)[0] == np.float32(O.tensor_amax(y, flags & fp4.RHT16, SEED))
 
 
 def test_edge_shapes():
