@@ -471,8 +471,12 @@ int mxfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b
     return launched(launch(fill_zero_kernel, (unsigned)grid, 256, (hipStream_t)stream, c, M * N));
   }
   const int64_t tiles_m = cdiv(M, kGemmBM), tiles_n = cdiv(N, kGemmBN);
+  // persistent: one workgroup per CU (its LDS ring fills most of the CU's),
+  // a multiple of 8 of them
   const int64_t slots = xcd_grid(tiles_m, tiles_n, kGemmSuperY, kGemmSuperX);
-  return launched(launch(mxfp4_gemm_kernel, (unsigned)slots, kGemmThreads, (hipStream_t)stream,
+  int64_t grid = slots < num_cus() ? slots : num_cus();
+  grid = (grid + kXcds - 1) / kXcds * kXcds;
+  return launched(launch(mxfp4_gemm_kernel, (unsigned)grid, kGemmThreads, (hipStream_t)stream,
                          a_codes, a_scales, bt_codes, bt_scales, M, N, K, c, (uint32_t)tiles_m,
                          (uint32_t)tiles_n));
 }
