@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_1d_kernel(
   constexpr int R = kAmaxThreads1d * kAmaxUnroll * 16 / (kThreads * 32);
   static_assert(R >= 1 && (R & (R - 1)) == 0, "amax chunk: a power-of-two number of 8 KiB chunks");
   const bool remap_on = !RHT && (G & 7) == 0;
-  const int top = (nchunks - 1) / (8 * R);             // -1 for an empty tensor
+  const int top = nchunks > 0 ? (nchunks - 1) / (8 * R) : -1;
   const int nvirt = remap_on ? 8 * R * (top + 1) : nchunks;
   // v = blockIdx.x + i G is this workgroup's i-th virtual chunk
   const int k0 = (int)blockIdx.x >> 3, x0 = (int)blockIdx.x & 7, kstep = G >> 3;
